@@ -1,0 +1,145 @@
+/*
+ * libw4a4 -- SVDQuant W4A4 quantized linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI.  Every tensor argument is a device pointer on the current HIP
+ * device, dense and row-major in the shape given; the caller owns every
+ * buffer.  All work is enqueued on `stream` (a hipStream_t passed as void*;
+ * NULL is the default stream).  No entry point allocates, frees or
+ * synchronizes.  Validation happens before any launch: a call that returns an
+ * error has launched nothing and written nothing.  Faults during execution
+ * surface at the caller's next synchronization.  Calls are thread-safe; the
+ * library keeps no state between calls.
+ *
+ * Formats (from the "SVDQuant W4A4" page, section "Checkpoint contract",
+ * configuration precision "nvfp4"):
+ *   FP4      E2M1, two values per byte, the even-k element in the low nibble;
+ *   scales   float8_e4m3fn bytes, one per 16 consecutive inputs along K;
+ *   bf16     IEEE bfloat16.
+ *
+ * Method (same page, sections "Overview" and "Runtime support"; rotation from
+ * the rotate notes, sections 2.1-2.2 and 3.3): y = x W^T is computed as
+ *   x_s   = x / smooth_factor                            (float32, IEEE)
+ *   v     = x_s @ H_B^T per B-block of K                 (optional rotation)
+ *   qact, ascales = per-16 group FP4 quantization of v   (amax/6 -> e4m3)
+ *   y     = bf16( (dequant(qact) @ dequant(qweight)^T) * wcscales * wtscale
+ *                 + (x_s @ proj_down) @ proj_up^T )
+ * with the weight-side smoothing and rotation folded into qweight offline.
+ */
+#ifndef W4A4_H_
+#define W4A4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A4_OK = 0,
+  W4A4_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  W4A4_ERR_SHAPE = 2,       /* a size is negative, K % 16 != 0, K % block != 0,
+                               or the workspace is too small                      */
+  W4A4_ERR_ALIGN = 3,       /* a pointer breaks its required alignment            */
+  W4A4_ERR_UNSUPPORTED = 4, /* hadamard_block not in {0,16,32,64,128} or R > 64   */
+  W4A4_ERR_HIP = 5          /* the HIP runtime reported an error at launch        */
+} w4a4_status;
+
+/* Largest supported correction rank R. */
+#define W4A4_MAX_RANK 64
+
+/* Human-readable name of a status code (static storage). */
+const char* w4a4_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int w4a4_version(void);
+
+/*
+ * Online activation quantizer ("SVDQuant W4A4" page, "Runtime support": BF16
+ * input; rotation: rotate notes 2.1 and 3.3, quantization fused with the
+ * rotation in one pass).  One HBM pass over x computes, per row m:
+ *   x_s  = float32(x) / float32(smooth_factor)                  (IEEE division)
+ *   v    = x_s, or x_s @ H_B^T on every contiguous B-block when hadamard_block
+ *          B > 0 (Sylvester order, butterfly spans 1,2,...,B/2, then one
+ *          multiply by float32(1/sqrt(B)))
+ *   per group g of 16:  s8 = e4m3(amax|v| / 6)  (round-nearest-even, saturating
+ *          at 448);  code = e2m1(v / e4m3_value(s8))  (round-nearest-even,
+ *          saturating at 6, sign of zero kept), all codes 0 when s8 == 0
+ *   lora_act = x_s @ proj_down       (unrotated x_s, float32 result)
+ *
+ *   x             bf16 [M, K]           16-byte aligned
+ *   smooth_factor bf16 [K]
+ *   proj_down     bf16 [K, R]           may be NULL when R == 0
+ *   M >= 0, K >= 16 with K % 16 == 0, 0 <= R <= 64
+ *   hadamard_block  0 (none) or 16, 32, 64, 128 with K % hadamard_block == 0
+ *   qact          u8   [M, K/2]  out    E2M1 pairs, 4-byte aligned
+ *   ascales       u8   [K/16, M] out    e4m3 bytes (layout mirrors wscales)
+ *   lora_act      f32  [M, R]    out    may be NULL when R == 0
+ * M == 0 is a valid empty call (nothing is launched).
+ */
+w4a4_status svdq_quantize_act(const void* x, const void* smooth_factor, const void* proj_down,
+                              int64_t M, int64_t K, int64_t R, int32_t hadamard_block,
+                              void* qact, void* ascales, float* lora_act, void* stream);
+
+/*
+ * Offline weight quantizer producing the checkpoint tensors ("SVDQuant W4A4"
+ * page, "Checkpoint contract": qweight (N, K/2) packed FP4, wscales (K/16, N)
+ * e4m3; rotate notes 2.1: weights are rotated offline, W' = R W).  Per row n:
+ *   w_s = float32(w) * float32(smooth_factor)    (exact for bf16 inputs)
+ *   v   = w_s, or w_s @ H_B^T per B-block (as in svdq_quantize_act)
+ *   per-16 group quantization exactly as in svdq_quantize_act.
+ *
+ *   w        bf16 [N, K]   16-byte aligned
+ *   smooth_factor bf16 [K]
+ *   qweight  u8   [N, K/2] out   4-byte aligned
+ *   wscales  u8   [K/16, N] out
+ */
+w4a4_status svdq_quantize_weight(const void* w, const void* smooth_factor, int64_t N, int64_t K,
+                                 int32_t hadamard_block, void* qweight, void* wscales, void* stream);
+
+/*
+ * Block-scaled FP4 GEMM with the low-rank correction fused in the epilogue
+ * ("SVDQuant W4A4" page, "Runtime support": NVFP4 GEMM followed by the BF16
+ * rank correction; "Checkpoint contract": proj_up, wcscales, wtscale):
+ *   y[m,n] = bf16( sum_k e2m1(qact[m,k]) e4m3(ascales[k/16,m])
+ *                        e2m1(qweight[n,k]) e4m3(wscales[k/16,n])
+ *                  * wcscales[n] * wtscale
+ *                  + sum_r lora_act[m,r] proj_up[n,r] )
+ * The products are exact; the sum is accumulated in float32 (matrix cores).
+ *
+ *   qact     u8   [M, K/2]   16-byte aligned     ascales u8 [K/16, M]
+ *   lora_act f32  [M, R]     may be NULL when R == 0
+ *   qweight  u8   [N, K/2]   16-byte aligned     wscales u8 [K/16, N]
+ *   proj_up  bf16 [N, R]     may be NULL when R == 0
+ *   wcscales bf16 [N]
+ *   wtscale  bf16 [1]        device scalar, read by the kernel
+ *   y        bf16 [M, N] out
+ */
+w4a4_status svdq_gemm_lowrank(const void* qact, const void* ascales, const float* lora_act,
+                              const void* qweight, const void* wscales, const void* proj_up,
+                              const void* wcscales, const void* wtscale,
+                              int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream);
+
+/* Bytes of workspace svdq_linear needs for these sizes (qact, ascales and
+ * lora_act, each 256-byte aligned).  Returns 0 for invalid sizes. */
+size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int64_t R);
+
+/*
+ * The whole layer: svdq_quantize_act into the workspace, then
+ * svdq_gemm_lowrank.  Arguments are the checkpoint tensors of the "SVDQuant
+ * W4A4" page's table plus the BF16 input x [M, K] and the output y [M, N].
+ * `workspace` is device memory of at least svdq_linear_workspace_bytes(M, K, R)
+ * bytes, 256-byte aligned; its contents need no initialisation and are
+ * overwritten.
+ */
+w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                        const void* proj_up, const void* smooth_factor, const void* wcscales,
+                        const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R,
+                        int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H_ */

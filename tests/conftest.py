@@ -1,0 +1,25 @@
+"""Shared test configuration.
+
+Tests marked ``gpu`` need an MI355X and the built HIP library; everything else
+runs on the CPU.
+"""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD MI355X GPU and the built libw4a4.so")
+
+
+@pytest.fixture(scope="session")
+def golden():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "rotate_notes_examples.json")) as f:
+        return json.load(f)

@@ -1,0 +1,113 @@
+"""Pins of the oracle's composition (block-scaled GEMM + epilogue).
+
+* A pure-Python triple loop of the block-scaled sum, decoding the packed bytes
+  with closed-form formulas (not the oracle's tables), on tiny shapes.
+* Replacing the quantizer by the identity reduces the layer to the unquantized
+  linear x W^T * wcscales * wtscale + low-rank term: this pins the smoothing
+  fold, the rotation fold (R^T R = I, rotate notes 2.1) and the epilogue.
+* On a synthetic workload, FP4 quantization noise lands in the expected band.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import formats, hadamard, linear, quant
+from w4a4_bit_quantized_amd import synth
+
+
+def _e2m1_closed(c):
+    s = -1.0 if c & 8 else 1.0
+    e, m = (c >> 1) & 3, c & 1
+    return s * (0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + 0.5 * m))
+
+
+def _e4m3_closed(b):
+    e, m = (b >> 3) & 15, b & 7
+    return m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+
+
+def _brute(qact, ascales, lora, qweight, wscales, pu, wcs, wts):
+    M, N, K = qact.shape[0], qweight.shape[0], qact.shape[1] * 2
+    R = pu.shape[1]
+    y = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            tot = 0.0
+            for g in range(K // 16):
+                part = 0.0
+                for k in range(16 * g, 16 * g + 16):
+                    ca = (int(qact[m, k // 2]) >> (4 * (k % 2))) & 0xF
+                    cw = (int(qweight[n, k // 2]) >> (4 * (k % 2))) & 0xF
+                    part += _e2m1_closed(ca) * _e2m1_closed(cw)
+                tot += _e4m3_closed(int(ascales[g, m])) * _e4m3_closed(int(wscales[g, n])) * part
+            y[m, n] = tot * float(wcs[n]) * float(wts[0]) + sum(float(lora[m, r]) * float(pu[n, r]) for r in range(R))
+    return y
+
+
+@pytest.mark.parametrize("M,K,N,R,B", [(1, 16, 1, 0, 0), (3, 32, 5, 1, 0), (8, 128, 8, 4, 16), (3, 128, 5, 4, 0)])
+def test_gemm_matches_block_scaled_triple_loop(M, K, N, R, B):
+    lay = synth.as_f32(synth.make_layer("tiny", seed=M * 100 + K, M=M, K=K, N=N, R=R, B=B))
+    qw, ws = quant.quantize_weight(lay["w"], lay["smooth_factor"], B)
+    qa, sa, lora = quant.quantize_act(lay["x"], lay["smooth_factor"], lay["proj_down"], B)
+    yb, y = linear.gemm_lowrank(qa, sa, lora, qw, ws, lay["proj_up"], lay["wcscales"], lay["wtscale"])
+    ref = _brute(qa, sa, lora, qw, ws, lay["proj_up"], lay["wcscales"], lay["wtscale"])
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(yb, formats.bf16_from_f64(ref))
+
+
+def test_rank_zero_has_no_lowrank_term():
+    lay = synth.as_f32(synth.make_layer("tiny", seed=3, M=4, K=64, N=6, R=0))
+    qw, ws = quant.quantize_weight(lay["w"], lay["smooth_factor"])
+    qa, sa, lora = quant.quantize_act(lay["x"], lay["smooth_factor"], lay["proj_down"])
+    _, y = linear.gemm_lowrank(qa, sa, lora, qw, ws, lay["proj_up"], lay["wcscales"], lay["wtscale"])
+    acc = linear.dequant(qa, sa) @ linear.dequant(qw, ws).T
+    assert np.array_equal(y, acc * lay["wcscales"].astype(np.float64)[None, :])
+
+
+@pytest.mark.parametrize("B", [0, 16, 128])
+def test_identity_quantizer_reduces_to_unquantized_linear(B):
+    """With the quantizer replaced by the identity the folds must cancel exactly (up to float32)."""
+    lay = synth.as_f32(synth.make_layer("tiny", seed=B + 1, M=6, K=256, N=7, R=5,
+                                        wcs="uniform"))
+    lam = lay["smooth_factor"]
+    xs = quant.smooth(lay["x"], lam)
+    a = hadamard.fwht_blocks(xs, B) if B else xs
+    wq = (lay["w"] * lam[None, :]).astype(np.float32)
+    wd = hadamard.fwht_blocks(wq, B) if B else wq
+    lora = xs.astype(np.float64) @ lay["proj_down"].astype(np.float64)
+    acc = a.astype(np.float64) @ wd.astype(np.float64).T
+    col = lay["wcscales"].astype(np.float64) * float(lay["wtscale"][0])
+    y_id = acc * col[None, :] + lora @ lay["proj_up"].astype(np.float64).T
+    ref = linear.unquantized_reference(lay["x"], lay["w"], lay["proj_down"], lay["proj_up"], lam,
+                                       lay["wcscales"], lay["wtscale"])
+    assert np.allclose(y_id, ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+
+def test_quantization_noise_is_in_the_fp4_band():
+    lay = synth.as_f32(synth.make_layer("tiny", seed=0))
+    layer = dict(zip(("qweight", "wscales"), quant.quantize_weight(lay["w"], lay["smooth_factor"])))
+    layer.update({k: lay[k] for k in ("proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale")})
+    yb, y, _ = linear.svdq_linear(lay["x"], layer)
+    ref = linear.unquantized_reference(lay["x"], lay["w"], lay["proj_down"], lay["proj_up"],
+                                       lay["smooth_factor"], lay["wcscales"], lay["wtscale"])
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    # E2M1 with amax/6 group scales keeps ~3 significant bits per operand: a
+    # dot product of two such operands lands at a few percent to ~20% error.
+    assert 0.01 < rel < 0.25
+    # a transposed weight-scale layout would be far worse
+    bad = dict(layer, wscales=np.ascontiguousarray(layer["wscales"][::-1]))
+    _, yb2, _ = linear.svdq_linear(lay["x"], bad)
+    assert np.linalg.norm(yb2 - ref) / np.linalg.norm(ref) > 2 * rel
+
+
+def test_svdq_linear_equals_two_steps():
+    lay = synth.as_f32(synth.make_layer("tiny", seed=2, M=5, K=64, N=9, R=3))
+    qw, ws = quant.quantize_weight(lay["w"], lay["smooth_factor"])
+    layer = dict(qweight=qw, wscales=ws, **{k: lay[k] for k in ("proj_down", "proj_up", "smooth_factor",
+                                                                 "wcscales", "wtscale")})
+    yb, y, (qa, sa, lora) = linear.svdq_linear(lay["x"], layer)
+    yb2, _ = linear.gemm_lowrank(qa, sa, lora, qw, ws, lay["proj_up"], lay["wcscales"], lay["wtscale"])
+    assert np.array_equal(yb, yb2)
+    assert math.isfinite(float(np.abs(y).max()))

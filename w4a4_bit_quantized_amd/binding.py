@@ -1,0 +1,209 @@
+"""ctypes binding of libw4a4 (include/w4a4.h).
+
+Argument marshalling only: dtype/device/contiguity checks on torch tensors,
+output allocation with torch, the current torch stream as the HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback.  The library is loaded on first use and a missing build raises.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+STATUS_NAMES = {0: "W4A4_OK", 1: "W4A4_ERR_NULL", 2: "W4A4_ERR_SHAPE", 3: "W4A4_ERR_ALIGN",
+                4: "W4A4_ERR_UNSUPPORTED", 5: "W4A4_ERR_HIP"}
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_c_p = ctypes.c_void_p
+
+# name -> (restype, argtypes), mirroring include/w4a4.h
+SIGNATURES = {
+    "w4a4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "w4a4_version": (ctypes.c_int, []),
+    "svdq_quantize_act": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p, _c_p]),
+    "svdq_quantize_weight": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+    "svdq_gemm_lowrank": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                         _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "svdq_linear_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
+    "svdq_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                   _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+}
+
+
+class W4A4Error(RuntimeError):
+    """A libw4a4 call returned a non-OK status (or the library is missing)."""
+
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path():
+    return os.environ.get("W4A4_LIBRARY", os.path.join(_HERE, "libw4a4.so"))
+
+
+def load_library():
+    """Load libw4a4.so (once) and declare its C signatures."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise W4A4Error(f"libw4a4.so is not built ({path}); run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(status, what):
+    if status != 0:
+        name = STATUS_NAMES.get(status, str(status))
+        msg = load_library().w4a4_status_string(status).decode()
+        raise W4A4Error(f"{what} failed: {name} ({msg})", status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t, name, dtypes, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _bytes_dtypes():
+    torch = _torch()
+    return (torch.uint8, torch.int8)
+
+
+def _scale_dtypes():
+    torch = _torch()
+    return (torch.uint8, torch.float8_e4m3fn)
+
+
+def svdq_linear_workspace_bytes(M, K, R):
+    return int(load_library().svdq_linear_workspace_bytes(int(M), int(K), int(R)))
+
+
+def svdq_quantize_act(x, smooth_factor, proj_down, hadamard_block=0):
+    """x (M, K) bf16 -> (qact (M, K/2) u8, ascales (K/16, M) u8, lora_act (M, R) f32)."""
+    torch = _torch()
+    lib = load_library()
+    x = _dev(x, "x", (torch.bfloat16,))
+    dev = x.device
+    M, K = x.shape
+    _dev(smooth_factor, "smooth_factor", (torch.bfloat16,), dev)
+    _dev(proj_down, "proj_down", (torch.bfloat16,), dev)
+    R = proj_down.shape[1]
+    qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    ascales = torch.empty((K // 16, M), dtype=torch.uint8, device=dev)
+    lora = torch.empty((M, R), dtype=torch.float32, device=dev)
+    st = lib.svdq_quantize_act(_ptr(x), _ptr(smooth_factor), _ptr(proj_down), M, K, R, int(hadamard_block),
+                               _ptr(qact), _ptr(ascales), _ptr(lora), _stream(dev))
+    _check(st, "svdq_quantize_act")
+    return qact, ascales, lora
+
+
+def svdq_quantize_weight(w, smooth_factor, hadamard_block=0):
+    """w (N, K) bf16 -> (qweight (N, K/2) u8, wscales (K/16, N) u8)."""
+    torch = _torch()
+    lib = load_library()
+    w = _dev(w, "w", (torch.bfloat16,))
+    dev = w.device
+    N, K = w.shape
+    _dev(smooth_factor, "smooth_factor", (torch.bfloat16,), dev)
+    qweight = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    wscales = torch.empty((K // 16, N), dtype=torch.uint8, device=dev)
+    st = lib.svdq_quantize_weight(_ptr(w), _ptr(smooth_factor), N, K, int(hadamard_block),
+                                  _ptr(qweight), _ptr(wscales), _stream(dev))
+    _check(st, "svdq_quantize_weight")
+    return qweight, wscales
+
+
+def svdq_gemm_lowrank(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, out=None):
+    """Block-scaled FP4 GEMM + epilogue -> y (M, N) bf16."""
+    torch = _torch()
+    lib = load_library()
+    qact = _dev(qact, "qact", _bytes_dtypes())
+    dev = qact.device
+    _dev(ascales, "ascales", _scale_dtypes(), dev)
+    _dev(lora_act, "lora_act", (torch.float32,), dev)
+    _dev(qweight, "qweight", _bytes_dtypes(), dev)
+    _dev(wscales, "wscales", _scale_dtypes(), dev)
+    _dev(proj_up, "proj_up", (torch.bfloat16,), dev)
+    _dev(wcscales, "wcscales", (torch.bfloat16,), dev)
+    _dev(wtscale, "wtscale", (torch.bfloat16,), dev)
+    M, K = qact.shape[0], qact.shape[1] * 2
+    N = qweight.shape[0]
+    R = proj_up.shape[1]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _dev(y, "y", (torch.bfloat16,), dev)
+    st = lib.svdq_gemm_lowrank(_ptr(qact), _ptr(ascales), _ptr(lora_act), _ptr(qweight), _ptr(wscales),
+                               _ptr(proj_up), _ptr(wcscales), _ptr(wtscale), M, N, K, R, _ptr(y), _stream(dev))
+    _check(st, "svdq_gemm_lowrank")
+    return y
+
+
+LAYER_KEYS = ("qweight", "wscales", "proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale")
+
+
+def svdq_linear(x, layer, hadamard_block=0, workspace=None, out=None):
+    """The whole W4A4 layer.  ``x`` (..., K) bf16; leading dims are flattened into M.
+
+    ``layer`` maps the checkpoint names (qweight, wscales, proj_down, proj_up,
+    smooth_factor, wcscales, wtscale) to device tensors.  ``workspace`` (u8,
+    at least svdq_linear_workspace_bytes bytes) and ``out`` may be passed to
+    avoid allocation.
+    """
+    torch = _torch()
+    lib = load_library()
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    _dev(x2, "x", (torch.bfloat16,))
+    dev = x2.device
+    M, K = x2.shape
+    t = {k: layer[k] for k in LAYER_KEYS}
+    _dev(t["qweight"], "qweight", _bytes_dtypes(), dev)
+    _dev(t["wscales"], "wscales", _scale_dtypes(), dev)
+    for k in ("proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale"):
+        _dev(t[k], k, (torch.bfloat16,), dev)
+    N = t["qweight"].shape[0]
+    R = t["proj_up"].shape[1]
+    need = int(lib.svdq_linear_workspace_bytes(M, K, R))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", (torch.uint8,), dev)
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _dev(y, "y", (torch.bfloat16,), dev)
+    st = lib.svdq_linear(_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]),
+                         _ptr(t["proj_up"]), _ptr(t["smooth_factor"]), _ptr(t["wcscales"]), _ptr(t["wtscale"]),
+                         M, N, K, R, int(hadamard_block), _ptr(y), _ptr(workspace),
+                         workspace.numel(), _stream(dev))
+    _check(st, "svdq_linear")
+    return y.reshape(*lead, N)

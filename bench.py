@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the SVDQuant W4A4 linear layer on one MI355X.
+
+One step is one whole layer call (svdq_linear: activation quantizer + block-
+scaled FP4 GEMM with the fused low-rank epilogue) over one batch of seeded
+synthetic input already resident in HBM.  The metric is effective TFLOP/s
+counted as 2*M*N*K per call.  Prints one JSON line.
+
+Default workload: the DiT MLP up-projection (M=4096, K=3072, N=12288, R=32),
+the compute-bound headline shape.  Other workloads: --workload NAME.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense f16/bf16 matrix peak
+PEAK_FP4_MFMA_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dit_mlp_up")
+    ap.add_argument("--sets", type=int, default=0, help="independent input sets cycled (0: enough to exceed 2x the MALL)")
+    ap.add_argument("--graph", action="store_true", help="replay the timed steps from a captured HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--calib-copy", action="store_true", help="also run one 512 MiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def sha_of(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gemm": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
+    "quantize": ["w4a4_bit_quantized_amd/csrc/quantize.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
+}
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None if stale/missing."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(f"{kernel}:{workload}")
+    if not ent or ent.get("source_sha") != sha_of(KERNEL_SOURCES[kernel]):
+        return None
+    return (ent["fetch_kib"] + ent["write_kib"]) * 1024.0 * ent["factor"]
+
+
+def cpu_baseline(spec_name, cpu_rows, seconds):
+    """The oracle (CPU, NumPy) on a bounded row sample of the same workload."""
+    import numpy as np
+    from oracle import linear as olinear
+    from oracle import quant as oquant
+    from w4a4_bit_quantized_amd import synth
+    lay = synth.make_layer(spec_name, seed=0)
+    f = synth.as_f32(lay)
+    qw, ws = oquant.quantize_weight(f["w"], f["smooth_factor"], lay["B"])  # offline, untimed
+    rows = min(cpu_rows, lay["M"])
+    layer = dict(qweight=qw, wscales=ws, **{k: f[k] for k in ("proj_down", "proj_up", "smooth_factor", "wcscales",
+                                                              "wtscale")})
+    x = np.ascontiguousarray(f["x"][:rows])
+    reps, t_total = 0, 0.0
+    while reps == 0 or t_total < seconds:
+        t0 = time.perf_counter()
+        olinear.svdq_linear(x, layer, lay["B"])
+        t_total += time.perf_counter() - t0
+        reps += 1
+    t = t_total / reps
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    flops = 2.0 * rows * lay["N"] * lay["K"]
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows} of {lay['M']} rows of {spec_name} (K={lay['K']}, N={lay['N']}, R={lay['R']}), "
+                      f"whole layer (smooth, rotate, quantize, dequantize, float64 GEMM, epilogue), "
+                      f"mean of {reps} runs, {t:.3f} s each; weight quantization untimed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer's multi-GPU sharding is "
+              f"design-only: see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import ctypes
+    import numpy as np
+    import torch
+
+    import w4a4_bit_quantized_amd as w4
+    from w4a4_bit_quantized_amd import binding, synth
+
+    if not os.path.exists(binding.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    lib = w4.load_library()
+    spec = synth.WORKLOADS[args.workload]
+    M, K, N, R, B = spec["M"], spec["K"], spec["N"], spec["R"], spec["B"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    per_set = M * K * 2 + N * K // 2 + N * K // 16 + M * N * 2 + w4.svdq_linear_workspace_bytes(M, K, R)
+    nsets = args.sets or max(1, -(-2 * MALL_BYTES // per_set))
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sets = []
+    for s in range(nsets):
+        lay = synth.make_layer(args.workload, seed=s)
+        wdev = bf(lay["w"])
+        lam = bf(lay["smooth_factor"])
+        qw, ws = w4.svdq_quantize_weight(wdev, lam, B)  # offline weight quantization on the GPU
+        del wdev
+        t = dict(x=bf(lay["x"]), qweight=qw, wscales=ws, proj_down=bf(lay["proj_down"]), proj_up=bf(lay["proj_up"]),
+                 smooth_factor=lam, wcscales=bf(lay["wcscales"]), wtscale=bf(lay["wtscale"]))
+        t["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        nbytes = w4.svdq_linear_workspace_bytes(M, K, R)
+        t["ws"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        # workspace views used by the two-entry-point breakdown loop (same layout as svdq_linear's)
+        a256 = lambda v: (v + 255) // 256 * 256
+        t["qact"] = t["ws"][: M * K // 2]
+        t["ascales"] = t["ws"][a256(M * K // 2): a256(M * K // 2) + K // 16 * M]
+        off = a256(M * K // 2) + a256(K // 16 * M)
+        t["lora"] = t["ws"][off: off + M * R * 4].view(torch.float32)
+        sets.append(t)
+        del lay
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda tt: ctypes.c_void_p(tt.data_ptr())
+    lin_args = [(P(t["x"]), P(t["qweight"]), P(t["wscales"]), P(t["proj_down"]), P(t["proj_up"]),
+                 P(t["smooth_factor"]), P(t["wcscales"]), P(t["wtscale"]), M, N, K, R, B, P(t["y"]), P(t["ws"]),
+                 t["ws"].numel(), sp) for t in sets]
+    q_args = [(P(t["x"]), P(t["smooth_factor"]), P(t["proj_down"]), M, K, R, B, P(t["qact"]), P(t["ascales"]),
+               P(t["lora"]), sp) for t in sets]
+    g_args = [(P(t["qact"]), P(t["ascales"]), P(t["lora"]), P(t["qweight"]), P(t["wscales"]), P(t["proj_up"]),
+               P(t["wcscales"]), P(t["wtscale"]), M, N, K, R, P(t["y"]), sp) for t in sets]
+
+    def step(i):
+        st = lib.svdq_linear(*lin_args[i % nsets])
+        if st:
+            raise RuntimeError(f"svdq_linear failed with status {st}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream(dev)
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            gsp = ctypes.c_void_p(gs.cuda_stream)
+            with torch.cuda.graph(graph, stream=gs):
+                for i in range(args.steps):
+                    a = list(lin_args[i % nsets])
+                    a[-1] = gsp
+                    lib.svdq_linear(*a)
+        stream.wait_stream(gs)
+        torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel durations: the same two kernels through the two-entry-point form, HIP events between them
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        e0, e1, e2 = evs[i]
+        e0.record(stream)
+        lib.svdq_quantize_act(*q_args[i % nsets])
+        e1.record(stream)
+        lib.svdq_gemm_lowrank(*g_args[i % nsets])
+        e2.record(stream)
+    torch.cuda.synchronize()
+    q_us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1, _ in evs) / args.steps
+    g_us = 1e3 * sum(e1.elapsed_time(e2) for _, e1, e2 in evs) / args.steps
+
+    if args.calib_copy:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    flops = 2.0 * M * N * K
+    value = flops / (wall_ms * 1e-3) / 1e12
+    q_bytes = M * K * 2 + K * 2 + K * R * 2 + M * K // 2 + M * K // 16 + M * R * 4
+    g_bytes = M * K // 2 + M * K // 16 + M * R * 4 + N * K // 2 + N * K // 16 + N * R * 2 + N * 2 + M * N * 2
+    kernels = {
+        "quantize_act": {"avg_us": round(q_us, 3), "algorithmic_bytes": q_bytes,
+                         "achieved_GBps": round(q_bytes / (q_us * 1e-6) / 1e9, 1)},
+        "gemm_lowrank": {"avg_us": round(g_us, 3), "algorithmic_bytes": g_bytes, "flops": flops,
+                         "achieved_TFLOPs": round(flops / (g_us * 1e-6) / 1e12, 1),
+                         "achieved_GBps": round(g_bytes / (g_us * 1e-6) / 1e9, 1)},
+    }
+    compute_bound = M >= 256
+    if compute_bound:
+        ach = flops / (g_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_F16_MFMA_TFLOPS, 4), "kernel": "gemm_lowrank",
+                "frac_of_fp4_peak": round(ach / PEAK_FP4_MFMA_TFLOPS, 4)}
+    else:
+        ach = g_bytes / (g_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": "gemm_lowrank"}
+    tr = traffic_from_profile("gemm", args.workload)
+    roof["traffic"] = None if tr is None else round(tr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_rows, args.cpu_seconds)
+
+    line = {
+        "metric": "W4A4 linear effective TFLOP/s (2MNK) and % of FP4-MFMA/HBM roofline",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5), "gpu_ms_per_step": round(gpu_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "storage": "fp4 e2m1 + e4m3 per 16 (nvfp4)",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "K": K, "N": N, "R": R, "hadamard_block": B,
+                   "input_sets": nsets, "graph": bool(args.graph)},
+        "frac_of_fp4_peak": round(value / PEAK_FP4_MFMA_TFLOPS, 4),
+        "kernels": kernels, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

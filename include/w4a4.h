@@ -8,7 +8,10 @@
  * synchronizes.  Validation happens before any launch: a call that returns an
  * error has launched nothing and written nothing.  Faults during execution
  * surface at the caller's next synchronization.  Calls are thread-safe; the
- * library keeps no state between calls.
+ * library keeps no state between calls.  Checks run in this order: sizes
+ * (W4A4_ERR_SHAPE / W4A4_ERR_UNSUPPORTED), the empty call (M or N == 0 is
+ * valid, launches nothing and may pass NULL pointers), NULL pointers
+ * (W4A4_ERR_NULL), alignment (W4A4_ERR_ALIGN).
  *
  * Formats (from the "SVDQuant W4A4" page, section "Checkpoint contract",
  * configuration precision "nvfp4"):

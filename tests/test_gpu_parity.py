@@ -1,0 +1,226 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Bars:
+* activation / weight codes and e4m3 scale bytes: bit-exact;
+* lora_act: within the float32 accumulation bound of the hi/lo bf16 split;
+* bf16 outputs: relative Frobenius error <= 5e-3 and max |diff| <= 2e-2 max|y_ref|,
+  plus a per-element bound from float32 accumulation and bf16 rounding;
+* the error against the unquantized linear is printed, not gated.
+
+Every call goes through the C ABI (libw4a4.so) via the ctypes binding.
+"""
+
+import numpy as np
+import pytest
+
+import helpers as H
+from oracle import linear as olinear
+from oracle import quant as oquant
+from w4a4_bit_quantized_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w4():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import w4a4_bit_quantized_amd as w
+    w.load_library()
+    return w
+
+
+def _lora_bound(xs, pd, K):
+    b = np.abs(xs.astype(np.float64)) @ np.abs(pd.astype(np.float64))
+    n_adds = 2 * K // 32 + 64
+    return (2.0 ** -18 + n_adds * 2.0 ** -24) * b + 1e-30
+
+
+def _check_quant_act(w4, lay, rows=None):
+    import torch
+    f = synth.as_f32(lay)
+    x = H.to_dev_bf16(lay["x"])
+    qa, sa, lo = w4.svdq_quantize_act(x, H.to_dev_bf16(lay["smooth_factor"]), H.to_dev_bf16(lay["proj_down"]),
+                                      lay["B"])
+    torch.cuda.synchronize()
+    rows = np.arange(lay["M"]) if rows is None else rows
+    q_ref, s_ref, l_ref = oquant.quantize_act(f["x"][rows], f["smooth_factor"], f["proj_down"], lay["B"])
+    q_gpu = qa.cpu().numpy()[rows]
+    s_gpu = sa.cpu().numpy()[:, rows]
+    bad = np.argwhere(q_gpu != q_ref)
+    assert bad.size == 0, f"{len(bad)} code bytes differ, first at {bad[:3].tolist()}"
+    bad = np.argwhere(s_gpu != s_ref)
+    assert bad.size == 0, f"{len(bad)} scale bytes differ, first at {bad[:3].tolist()}"
+    if lay["R"]:
+        xs = oquant.smooth(f["x"][rows], f["smooth_factor"])
+        bound = _lora_bound(xs, f["proj_down"], lay["K"])
+        l_gpu = lo.cpu().numpy()[rows].astype(np.float64)
+        err = np.abs(l_gpu - l_ref)
+        assert np.all(err <= bound), f"lora_act error {err.max():.3e} above bound at {np.argmax(err - bound)}"
+    return qa, sa, lo
+
+
+QUANT_CASES = [
+    # (M, K, R, B)
+    (64, 256, 32, 0),      # tiny workload shape
+    (1, 16, 0, 0),         # single group, no low-rank branch
+    (17, 48, 5, 16),       # K % 32 == 16, ragged rows, odd rank, block 16
+    (130, 256, 32, 32),    # several row tiles + tail, block 32
+    (33, 512, 64, 64),     # maximum rank, block 64
+    (16, 384, 16, 128),    # block 128, three blocks
+    (20, 1024, 33, 128),   # rank not a multiple of 8 (scalar proj_down path)
+    (5, 80, 1, 16),        # rank 1
+    (48, 4096, 32, 0),     # long K, many waves per workgroup
+    (7, 16 * 1000, 8, 0),  # K not a multiple of the unit split
+]
+
+
+@pytest.mark.parametrize("M,K,R,B", QUANT_CASES)
+def test_quantize_act_parity(w4, M, K, R, B):
+    lay = synth.make_layer("tiny", seed=M * 7 + K, M=M, K=K, N=8, R=R, B=B)
+    _check_quant_act(w4, lay)
+
+
+@pytest.mark.parametrize("N,K,B", [(8, 256, 0), (1, 16, 0), (33, 48, 16), (130, 512, 128), (64, 1024, 64),
+                                   (200, 96, 32)])
+def test_quantize_weight_parity(w4, N, K, B):
+    import torch
+    lay = synth.make_layer("tiny", seed=N + K, M=4, K=K, N=N, R=4, B=B)
+    qw, ws = w4.svdq_quantize_weight(H.to_dev_bf16(lay["w"]), H.to_dev_bf16(lay["smooth_factor"]), B)
+    torch.cuda.synchronize()
+    q_ref, s_ref = H.oracle_weights(lay)
+    assert np.array_equal(qw.cpu().numpy(), q_ref)
+    assert np.array_equal(ws.cpu().numpy(), s_ref)
+
+
+def _check_gemm(w4, lay, rows=None, cols=None):
+    """GEMM fed with the oracle's quantized tensors; compared with the oracle's float64 result."""
+    import torch
+    f = synth.as_f32(lay)
+    qw, ws = H.oracle_weights(lay)
+    qa, sa, lo = oquant.quantize_act(f["x"], f["smooth_factor"], f["proj_down"], lay["B"])
+    lo32 = lo.astype(np.float32)
+    y = w4.svdq_gemm_lowrank(H.to_dev_u8(qa), H.to_dev_u8(sa), torch.from_numpy(lo32).cuda(), H.to_dev_u8(qw),
+                             H.to_dev_u8(ws), H.to_dev_bf16(lay["proj_up"]), H.to_dev_bf16(lay["wcscales"]),
+                             H.to_dev_bf16(lay["wtscale"]))
+    torch.cuda.synchronize()
+    yb_ref, y_ref = olinear.gemm_lowrank(qa, sa, lo32, qw, ws, f["proj_up"], f["wcscales"], f["wtscale"])
+    y_gpu = H.from_dev_bf16_f64(y)
+    H.assert_gates(y_gpu, y_ref, "gemm")
+    bound = H.accumulation_bound(qa, sa, lo32, qw, ws, f["proj_up"], f["wcscales"], f["wtscale"],
+                                 n_adds=lay["K"] // 4 + 4 * lay["R"] + 64)
+    err = np.abs(y_gpu - y_ref)
+    lim = 2.0 ** -8 * np.abs(y_ref) + bound + 1e-30
+    assert np.all(err <= lim), f"per-element bound broken: worst excess {np.max(err - lim):.3e}"
+    return y_gpu, y_ref
+
+
+GEMM_CASES = [
+    # (M, N, K, R)
+    (64, 256, 256, 32),
+    (1, 1, 16, 0),
+    (130, 200, 48, 5),
+    (257, 129, 384, 64),
+    (33, 300, 1024, 16),
+    (128, 128, 128, 32),
+    (16, 600, 5120, 32),
+    (200, 64, 3072, 1),
+]
+
+
+@pytest.mark.parametrize("M,N,K,R", GEMM_CASES)
+def test_gemm_lowrank_parity(w4, M, N, K, R):
+    lay = synth.make_layer("tiny", seed=M + N + K, M=M, K=K, N=N, R=R, B=0, wcs="uniform")
+    _check_gemm(w4, lay)
+
+
+@pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 0), (37, 70, 256, 32, 128), (3, 40, 48, 3, 16),
+                                       (150, 260, 512, 64, 64)])
+def test_linear_parity(w4, M, N, K, R, B):
+    import torch
+    lay = synth.make_layer("tiny", seed=11 + M, M=M, K=K, N=N, R=R, B=B, wcs="uniform")
+    qw, ws = H.oracle_weights(lay)
+    y = w4.svdq_linear(H.to_dev_bf16(lay["x"]), H.device_layer(lay, qw, ws), hadamard_block=B)
+    torch.cuda.synchronize()
+    yb_ref, y_ref, _ = H.oracle_linear_rows(lay, qw, ws)
+    H.assert_gates(H.from_dev_bf16_f64(y), y_ref, "svdq_linear")
+
+
+@pytest.mark.parametrize("name", synth.ORDER)
+def test_workload_full_size(w4, name):
+    """Full-size run of each workload; outputs checked on sampled rows and columns."""
+    import torch
+    lay = synth.make_layer(name, seed=0)
+    M, N, K, B = lay["M"], lay["N"], lay["K"], lay["B"]
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(M, min(M, 48), replace=False))
+    cols = np.sort(rng.choice(N, min(N, 256), replace=False))
+    # weights quantized on the GPU at full size, checked bit-exact on the sampled rows
+    qw_d, ws_d = w4.svdq_quantize_weight(H.to_dev_bf16(lay["w"]), H.to_dev_bf16(lay["smooth_factor"]), B)
+    f = synth.as_f32(lay)
+    qw_ref, ws_ref = oquant.quantize_weight(f["w"][cols], f["smooth_factor"], B)
+    torch.cuda.synchronize()
+    assert np.array_equal(qw_d.cpu().numpy()[cols], qw_ref)
+    assert np.array_equal(ws_d.cpu().numpy()[:, cols], ws_ref)
+    # activation quantizer at full size, checked bit-exact on sampled rows
+    _check_quant_act(w4, lay, rows)
+    # whole layer at full size
+    layer = H.device_layer(lay, np.zeros((1, 1), np.uint8), np.zeros((1, 1), np.uint8))
+    layer["qweight"], layer["wscales"] = qw_d, ws_d
+    y = w4.svdq_linear(H.to_dev_bf16(lay["x"]), layer, hadamard_block=B)
+    torch.cuda.synchronize()
+    y_gpu = H.from_dev_bf16_f64(y)[np.ix_(rows, cols)]
+    sub = dict(lay, x=lay["x"][rows], w=lay["w"][cols], proj_up=lay["proj_up"][cols], wcscales=lay["wcscales"][cols],
+               M=len(rows), N=len(cols))
+    _, y_ref, _ = H.oracle_linear_rows(sub, qw_ref, ws_ref)
+    rel, mx = H.assert_gates(y_gpu, y_ref, name)
+    ref_unq = olinear.unquantized_reference(f["x"][rows], f["w"][cols], f["proj_down"], f["proj_up"][cols],
+                                            f["smooth_factor"], f["wcscales"][cols], f["wtscale"])
+    rel_unq = np.linalg.norm(y_gpu - ref_unq) / np.linalg.norm(ref_unq)
+    print(f"\n{name}: parity rel_fro={rel:.2e} max={mx:.2e}; vs unquantized linear (reported, not gated) "
+          f"rel_fro={rel_unq:.3f}")
+
+
+def test_empty_batch(w4):
+    import torch
+    lay = synth.make_layer("tiny", seed=1, M=4, K=64, N=8, R=4)
+    qw, ws = H.oracle_weights(lay)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    y = w4.svdq_linear(x, H.device_layer(lay, qw, ws))
+    assert tuple(y.shape) == (0, 8)
+
+
+def test_special_values(w4):
+    """Zero groups, negative zeros, saturating groups and infinities: codes and scales bit-exact."""
+    lay = synth.make_layer("tiny", seed=5, M=8, K=64, N=8, R=4)
+    x = synth.bits_to_f32(lay["x"]).copy()
+    x[0, :] = 0.0
+    x[1, :16] = -0.0
+    x[1, 16:] = np.float32(60000.0)
+    x[2, 5] = np.inf
+    x[3, 20] = -np.inf
+    x[4, :16] = np.float32(2.0 ** -120)
+    lay["x"] = synth.to_bf16_bits(x)
+    lay["R"] = 0
+    lay["proj_down"] = lay["proj_down"][:, :0]
+    _check_quant_act(w4, lay)
+
+
+def test_deterministic(w4):
+    import torch
+    lay = synth.make_layer("tiny", seed=9, M=300, K=1024, N=520, R=32)
+    qw, ws = H.oracle_weights(lay)
+    layer = H.device_layer(lay, qw, ws)
+    x = H.to_dev_bf16(lay["x"])
+    y1 = w4.svdq_linear(x, layer).clone()
+    y2 = w4.svdq_linear(x, layer)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_error_status_through_binding(w4):
+    lay = synth.make_layer("tiny", seed=1, M=4, K=64, N=8, R=4)
+    qw, ws = H.oracle_weights(lay)
+    with pytest.raises(w4.W4A4Error) as e:
+        w4.svdq_linear(H.to_dev_bf16(lay["x"]), H.device_layer(lay, qw, ws), hadamard_block=8)
+    assert e.value.status == 4

@@ -1,0 +1,145 @@
+// C-ABI entry points of libw4a4: argument validation, then kernel launches.
+// The contract of each entry point is documented in include/w4a4.h.
+#include "w4a4.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;  // sizes are indexed with 32-bit ints in the kernels
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+w4a4_status check_k_rank_block(int64_t K, int64_t R, int32_t hb) {
+  if (hb != 0 && hb != 16 && hb != 32 && hb != 64 && hb != 128) return W4A4_ERR_UNSUPPORTED;
+  if (R > W4A4_MAX_RANK) return W4A4_ERR_UNSUPPORTED;
+  if (K < 16 || K % 16 != 0 || K > kMaxDim || R < 0) return W4A4_ERR_SHAPE;
+  if (hb != 0 && K % hb != 0) return W4A4_ERR_SHAPE;
+  return W4A4_OK;
+}
+
+w4a4_status from_hip(hipError_t e) { return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP; }
+
+// Order of checks everywhere: sizes, then the empty call (M or N == 0: valid, launches
+// nothing, pointers may be NULL), then NULL pointers, then alignment.
+w4a4_status validate_quantize_act(const void* x, const void* lam, const void* pd, int64_t M, int64_t K, int64_t R,
+                                  int32_t hb, const void* qact, const void* ascales, const float* lora) {
+  w4a4_status st = check_k_rank_block(K, R, hb);
+  if (st != W4A4_OK) return st;
+  if (M < 0 || M > kMaxDim) return W4A4_ERR_SHAPE;
+  if (M == 0) return W4A4_OK;
+  if (!x || !lam || !qact || !ascales) return W4A4_ERR_NULL;
+  if (R > 0 && (!pd || !lora)) return W4A4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(lam, 16) || !aligned(qact, 4)) return W4A4_ERR_ALIGN;
+  if (R > 0 && (!aligned(pd, 2) || !aligned(lora, 4))) return W4A4_ERR_ALIGN;
+  return W4A4_OK;
+}
+
+w4a4_status validate_gemm(const void* qact, const void* ascales, const float* lora, const void* qweight,
+                          const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
+                          int64_t M, int64_t N, int64_t K, int64_t R, const void* y) {
+  w4a4_status st = check_k_rank_block(K, R, 0);
+  if (st != W4A4_OK) return st;
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return W4A4_ERR_SHAPE;
+  if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return W4A4_ERR_SHAPE;  // 1-D grid of output tiles
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!qact || !ascales || !qweight || !wscales || !wcscales || !wtscale || !y) return W4A4_ERR_NULL;
+  if (R > 0 && (!lora || !proj_up)) return W4A4_ERR_NULL;
+  if (!aligned(qact, 16) || !aligned(qweight, 16)) return W4A4_ERR_ALIGN;
+  if (!aligned(wcscales, 2) || !aligned(wtscale, 2) || !aligned(y, 2)) return W4A4_ERR_ALIGN;
+  if (R > 0 && (!aligned(lora, 4) || !aligned(proj_up, 2))) return W4A4_ERR_ALIGN;
+  return W4A4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a4_status_string(int status) {
+  switch (status) {
+    case W4A4_OK: return "ok";
+    case W4A4_ERR_NULL: return "a required pointer is NULL";
+    case W4A4_ERR_SHAPE: return "invalid sizes (negative, K % 16 != 0, K % hadamard_block != 0, or workspace too small)";
+    case W4A4_ERR_ALIGN: return "a pointer breaks its required alignment";
+    case W4A4_ERR_UNSUPPORTED: return "unsupported hadamard_block or rank above the compiled maximum";
+    case W4A4_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int w4a4_version(void) { return 100; }
+
+w4a4_status svdq_quantize_act(const void* x, const void* smooth_factor, const void* proj_down, int64_t M, int64_t K,
+                              int64_t R, int32_t hadamard_block, void* qact, void* ascales, float* lora_act,
+                              void* stream) {
+  w4a4_status st = validate_quantize_act(x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales, lora_act);
+  if (st != W4A4_OK || M == 0) return st;
+  (void)hipGetLastError();  // clear a stale error so it is not reported as ours
+  return from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales,
+                                        lora_act, static_cast<hipStream_t>(stream)));
+}
+
+w4a4_status svdq_quantize_weight(const void* w, const void* smooth_factor, int64_t N, int64_t K,
+                                 int32_t hadamard_block, void* qweight, void* wscales, void* stream) {
+  w4a4_status st = check_k_rank_block(K, 0, hadamard_block);
+  if (st != W4A4_OK) return st;
+  if (N < 0 || N > kMaxDim) return W4A4_ERR_SHAPE;
+  if (N == 0) return W4A4_OK;
+  if (!w || !smooth_factor || !qweight || !wscales) return W4A4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(smooth_factor, 16) || !aligned(qweight, 4)) return W4A4_ERR_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(w4a4::launch_quantize(false, w, smooth_factor, nullptr, N, K, 0, hadamard_block, qweight, wscales,
+                                        nullptr, static_cast<hipStream_t>(stream)));
+}
+
+w4a4_status svdq_gemm_lowrank(const void* qact, const void* ascales, const float* lora_act, const void* qweight,
+                              const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
+                              int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream) {
+  w4a4_status st = validate_gemm(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  (void)hipGetLastError();
+  return from_hip(w4a4::launch_gemm(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, M, N, K,
+                                    R, y, static_cast<hipStream_t>(stream)));
+}
+
+size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+  if (M < 0 || M > kMaxDim || check_k_rank_block(K, R, 0) != W4A4_OK) return 0;
+  const size_t m = (size_t)M, k = (size_t)K, r = (size_t)R;
+  return align256(m * k / 2) + align256(k / 16 * m) + align256(m * r * sizeof(float));
+}
+
+w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                        const void* proj_up, const void* smooth_factor, const void* wcscales, const void* wtscale,
+                        int64_t M, int64_t N, int64_t K, int64_t R, int32_t hadamard_block, void* y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  w4a4_status st = check_k_rank_block(K, R, hadamard_block);
+  if (st != W4A4_OK) return st;
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return W4A4_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!x || !qweight || !wscales || !smooth_factor || !wcscales || !wtscale || !y) return W4A4_ERR_NULL;
+  if (R > 0 && (!proj_down || !proj_up)) return W4A4_ERR_NULL;
+  if (!workspace) return W4A4_ERR_NULL;
+  const size_t need = svdq_linear_workspace_bytes(M, K, R);
+  if (workspace_bytes < need) return W4A4_ERR_SHAPE;
+  if (!aligned(workspace, 256)) return W4A4_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void* qact = ws;
+  void* ascales = ws + align256((size_t)M * K / 2);
+  float* lora = R > 0 ? reinterpret_cast<float*>(ws + align256((size_t)M * K / 2) + align256((size_t)K / 16 * M))
+                      : nullptr;
+  st = validate_quantize_act(x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales, lora);
+  if (st != W4A4_OK) return st;
+  st = validate_gemm(qact, ascales, lora, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
+  if (st != W4A4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  st = from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales, lora, s));
+  if (st != W4A4_OK) return st;
+  return from_hip(w4a4::launch_gemm(qact, ascales, lora, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y, s));
+}
+
+}  // extern "C"

@@ -95,6 +95,19 @@ __device__ __forceinline__ uint32_t e4m3_to_h2bits(uint32_t b) {
   return hb | (hb << 16);
 }
 
+// Two e4m3 bytes (bits 0-15 of w) -> two f16 (exact), packed in one dword.
+__device__ __forceinline__ uint32_t e4m3x2_to_h2bits(uint32_t w) {
+  float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));  // exact: no rounding occurs
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// {s, s} from the low (hi == 0) or high half of a packed f16 pair.
+__device__ __forceinline__ half2_t scale_pair(uint32_t packed, int hi) {
+  half2_t p = __builtin_bit_cast(half2_t, packed);
+  return hi ? half2_t{p[1], p[1]} : half2_t{p[0], p[0]};
+}
+
 // Order LDS traffic between lanes of one wave (wave-private LDS regions).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -134,6 +134,17 @@ def test_gemm_lowrank_parity(w4, M, N, K, R):
     _check_gemm(w4, lay)
 
 
+GEMM_VARIANTS = ["2x2x4x4", "2x2x4x3", "2x2x4x2", "2x2x2x2", "4x2x2x4", "2x4x4x2", "4x2x2x3"]
+
+
+@pytest.mark.parametrize("variant", GEMM_VARIANTS)
+def test_gemm_every_tile_variant(w4, variant, monkeypatch):
+    """Each compiled tile layout, forced through W4A4_GEMM_TILE, on a shape with ragged edges."""
+    monkeypatch.setenv("W4A4_GEMM_TILE", variant)
+    lay = synth.make_layer("tiny", seed=31, M=300, K=640, N=520, R=32, B=0, wcs="uniform")
+    _check_gemm(w4, lay)
+
+
 @pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 0), (37, 70, 256, 32, 128), (3, 40, 48, 3, 16),
                                        (150, 260, 512, 64, 64)])
 def test_linear_parity(w4, M, N, K, R, B):

@@ -42,74 +42,130 @@ namespace {
 
 constexpr int BK = 128;            // K columns per stage (8 groups of 16)
 constexpr int CODE_STRIDE = 80;    // LDS bytes per code row: 64 data + 16 pad (conflict-free b128 reads)
-constexpr int SCALE_STRIDE = 24;   // LDS bytes per scale row: 8 f16 + 8 pad (conflict-free b64 reads)
 
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 struct Tile {
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;
-  static constexpr int ROWS = BM + BN;  // A rows then B rows in LDS
-  static constexpr int CHUNKS = ROWS * 4;  // 16-byte code chunks per stage
-  static_assert(CHUNKS % THREADS == 0, "code chunks must split evenly over the threads");
-  static constexpr int CHUNKS_PER_THREAD = CHUNKS / THREADS;
-  static constexpr int SCALE_ROWS_PER_THREAD = (ROWS + THREADS - 1) / THREADS;
-  static constexpr int STAGE_BYTES = ROWS * (CODE_STRIDE + SCALE_STRIDE);
-  static constexpr int OUT_BYTES = BM * BN * 2;  // bf16 tile for the transposed store
-  static constexpr int LDS_BYTES = (2 * STAGE_BYTES > OUT_BYTES ? 2 * STAGE_BYTES : OUT_BYTES);
+  static constexpr int ROWS = BM + BN;  // activation rows, then weight rows, in LDS
+  static constexpr int A_CPT = (BM * 4 + THREADS - 1) / THREADS;  // 16-byte code chunks per thread
+  static constexpr int B_CPT = (BN * 4 + THREADS - 1) / THREADS;
+  static constexpr int SA_PT = (2 * BM + THREADS - 1) / THREADS;  // (group, 4-row quad) scale words per thread
+  static constexpr int SB_PT = (2 * BN + THREADS - 1) / THREADS;
+  static constexpr int SCALE_BYTES = 8 * ROWS * 2;  // f16 scales laid out [group][row]
+  static constexpr int STAGE_BYTES = ROWS * CODE_STRIDE + SCALE_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
 };
 
+// Global -> register -> LDS staging of one K-step.  Per-thread offsets are loop invariant;
+// each K-step only moves the uniform base pointers.  Rows past M (or N) read a clamped valid
+// row: they feed only output rows (columns) that are never stored.  Columns past K, which
+// would mix into valid outputs, are zeroed in the one partial K-step.
 template <class T, bool VEC16>
 struct Stager {
-  u32x4_t codes[T::CHUNKS_PER_THREAD];
-  uint32_t sc[T::SCALE_ROWS_PER_THREAD][2];  // 8 raw e4m3 bytes per staged row
+  uint32_t a_off[T::A_CPT], b_off[T::B_CPT];  // row * kbytes + 16 * piece within the tile
+  uint32_t s_a[T::SA_PT], s_b[T::SB_PT];      // group * rows_total + first row of the quad (clamped)
+  u32x4_t a_codes[T::A_CPT], b_codes[T::B_CPT];
+  uint32_t a_sc[T::SA_PT], b_sc[T::SB_PT];    // 4 raw e4m3 bytes: one group, 4 consecutive rows
 
-  // Branch-free: every load reads a valid address (row 0 / group 0 when out of range) and the
-  // value is zeroed afterwards, so all loads issue back to back with a single wait at the use.
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ qw,
-                                       const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sw, int M, int N,
-                                       int m0, int n0, int kt, int kbytes, int groups, int t) {
-    const int kb0 = kt * (BK / 2);
+  // Scale words: index i = group * (rows / 4) + quad, so consecutive threads read consecutive
+  // bytes of one group row of the (K/16, rows) scale tensor.
+  __device__ __forceinline__ static uint32_t scale_word_off(int i, int rows, int rows_valid, int rows_total) {
+    const int quads = rows / 4;
+    const int g = min(i / quads, 7);
+    const int r = min(4 * (i % quads), ((rows_valid + 3) & ~3) - 4);
+    return (uint32_t)(g * rows_total + r);
+  }
+
+  __device__ __forceinline__ void init(int rows_a, int rows_b, int M, int N, int kbytes, int t) {
 #pragma unroll
-    for (int j = 0; j < T::CHUNKS_PER_THREAD; ++j) {
+    for (int j = 0; j < T::A_CPT; ++j) {
       const int c = t + T::THREADS * j;
-      const int row = c >> 2, piece = c & 3;
-      const bool is_a = row < T::BM;
-      const int gr = is_a ? m0 + row : n0 + (row - T::BM);
-      const int lim = is_a ? M : N;
-      const uint8_t* base = is_a ? qa : qw;
-      const int off = kb0 + 16 * piece;
-      if (VEC16) {
-        const bool ok = gr < lim && off + 16 <= kbytes;
-        u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + (ok ? (size_t)gr * kbytes + off : 0));
-        codes[j] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+      const int row = min(c >> 2, rows_a - 1);
+      a_off[j] = (uint32_t)row * (uint32_t)kbytes + 16u * (uint32_t)(c & 3);
+    }
+#pragma unroll
+    for (int j = 0; j < T::B_CPT; ++j) {
+      const int c = t + T::THREADS * j;
+      const int row = min(c >> 2, rows_b - 1);
+      b_off[j] = (uint32_t)row * (uint32_t)kbytes + 16u * (uint32_t)(c & 3);
+    }
+#pragma unroll
+    for (int j = 0; j < T::SA_PT; ++j) s_a[j] = scale_word_off(t + T::THREADS * j, T::BM, rows_a, M);
+#pragma unroll
+    for (int j = 0; j < T::SB_PT; ++j) s_b[j] = scale_word_off(t + T::THREADS * j, T::BN, rows_b, N);
+  }
+
+  template <bool TAIL>
+  __device__ __forceinline__ void load_codes(const uint8_t* __restrict__ base, const uint32_t* off, u32x4_t* dst,
+                                             int n, int kb0, int kbytes, int t) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) {
+      const uint8_t* p = base + off[j];
+      if (VEC16 && !TAIL) {
+        dst[j] = *reinterpret_cast<const u32x4_t*>(p);
       } else {
-        const bool ok_lo = gr < lim && off + 8 <= kbytes;
-        const bool ok_hi = gr < lim && off + 16 <= kbytes;
-        u32x2_t lo = *reinterpret_cast<const u32x2_t*>(base + (ok_lo ? (size_t)gr * kbytes + off : 0));
-        u32x2_t hi = *reinterpret_cast<const u32x2_t*>(base + (ok_hi ? (size_t)gr * kbytes + off + 8 : 0));
-        codes[j] = u32x4_t{ok_lo ? lo[0] : 0u, ok_lo ? lo[1] : 0u, ok_hi ? hi[0] : 0u, ok_hi ? hi[1] : 0u};
+        const int col = kb0 + 16 * ((t + T::THREADS * j) & 3);  // byte column of the chunk
+        const bool ok_lo = !TAIL || col + 8 <= kbytes;
+        const bool ok_hi = !TAIL || col + 16 <= kbytes;
+        u32x2_t lo = *reinterpret_cast<const u32x2_t*>(ok_lo ? p : base - kb0);
+        u32x2_t hi = *reinterpret_cast<const u32x2_t*>(ok_hi ? p + 8 : base - kb0);
+        dst[j] = u32x4_t{ok_lo ? lo[0] : 0u, ok_lo ? lo[1] : 0u, ok_hi ? hi[0] : 0u, ok_hi ? hi[1] : 0u};
       }
     }
-    const int g0 = kt * (BK / 16);
+  }
+
+  // SC4: every quad is 4 valid, dword-aligned rows (M and N multiples of 4); otherwise bytes.
+  template <bool SC4>
+  __device__ __forceinline__ static void load_scales(const uint8_t* __restrict__ base, const uint32_t* off,
+                                                     uint32_t* dst, int n, int rows_valid, int rows_total,
+                                                     int row0) {
 #pragma unroll
-    for (int j = 0; j < T::SCALE_ROWS_PER_THREAD; ++j) {
-      const int row = t + T::THREADS * j;
-      const bool is_a = row < T::BM;
-      const int gr = is_a ? m0 + row : n0 + (row - T::BM);
-      const int lim = is_a ? M : N;
-      const uint8_t* s = is_a ? sa : sw;
-      const bool row_ok = row < T::ROWS && gr < lim;
-      uint32_t w0 = 0u, w1 = 0u;
+    for (int j = 0; j < n; ++j) {
+      if (SC4) {
+        dst[j] = *reinterpret_cast<const uint32_t*>(base + off[j]);
+      } else {
+        const int r = (int)(off[j] % (uint32_t)rows_total);  // first row of the quad within the tile
+        uint32_t w = 0u;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const bool ok = row_ok && g0 + g < groups;
-        uint32_t b = s[ok ? (size_t)(g0 + g) * lim + gr : 0];
-        b = ok ? b : 0u;
-        if (g < 4) w0 |= b << (8 * g); else w1 |= b << (8 * (g - 4));
+        for (int e = 0; e < 4; ++e) w |= (uint32_t)base[off[j] - r + min(r + e, rows_valid - 1)] << (8 * e);
+        dst[j] = w;
       }
-      sc[j][0] = w0;
-      sc[j][1] = w1;
+      (void)row0;
+    }
+  }
+
+  template <bool TAIL, bool SC4>
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ qw,
+                                       const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sw, int M, int N,
+                                       int m0, int n0, int rows_a, int rows_b, int kt, int kbytes, int groups,
+                                       int t) {
+    const int kb0 = kt * (BK / 2);
+    load_codes<TAIL>(qa + (size_t)m0 * kbytes + kb0, a_off, a_codes, T::A_CPT, kb0, kbytes, t);
+    load_codes<TAIL>(qw + (size_t)n0 * kbytes + kb0, b_off, b_codes, T::B_CPT, kb0, kbytes, t);
+    const int g0 = kt * (BK / 16);
+    if (!TAIL) {
+      load_scales<SC4>(sa + (size_t)g0 * M + m0, s_a, a_sc, T::SA_PT, rows_a, M, m0);
+      load_scales<SC4>(sw + (size_t)g0 * N + n0, s_b, b_sc, T::SB_PT, rows_b, N, n0);
+    } else {
+      // Partial K-step: groups past K read the last group (a finite scale; their codes are 0).
+      tail_scales(sa, s_a, a_sc, T::SA_PT, g0, groups, rows_a, M, m0);
+      tail_scales(sw, s_b, b_sc, T::SB_PT, g0, groups, rows_b, N, n0);
+    }
+  }
+
+  __device__ __forceinline__ static void tail_scales(const uint8_t* __restrict__ s, const uint32_t* off, uint32_t* dst,
+                                                     int n, int g0, int groups, int rows_valid, int rows_total,
+                                                     int row0) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) {
+      const int g = (int)(off[j] / (uint32_t)rows_total), r = (int)(off[j] % (uint32_t)rows_total);
+      const uint8_t* b = s + (size_t)min(g0 + g, groups - 1) * rows_total + row0;
+      uint32_t w = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w |= (uint32_t)b[min(r + e, rows_valid - 1)] << (8 * e);
+      dst[j] = w;
     }
   }
 
@@ -117,27 +173,49 @@ struct Stager {
     uint8_t* codes_lds = stage;
     uint8_t* scale_lds = stage + T::ROWS * CODE_STRIDE;
 #pragma unroll
-    for (int j = 0; j < T::CHUNKS_PER_THREAD; ++j) {
+    for (int j = 0; j < T::A_CPT; ++j) {
       const int c = t + T::THREADS * j;
-      *reinterpret_cast<u32x4_t*>(codes_lds + (c >> 2) * CODE_STRIDE + 16 * (c & 3)) = codes[j];
+      if ((T::BM * 4) % T::THREADS == 0 || c < T::BM * 4)
+        *reinterpret_cast<u32x4_t*>(codes_lds + (c >> 2) * CODE_STRIDE + 16 * (c & 3)) = a_codes[j];
     }
 #pragma unroll
-    for (int j = 0; j < T::SCALE_ROWS_PER_THREAD; ++j) {
-      const int row = t + T::THREADS * j;
-      if (row < T::ROWS) {
-        u32x2_t lo, hi;
-        lo[0] = e4m3x2_to_h2bits(sc[j][0]);
-        lo[1] = e4m3x2_to_h2bits(sc[j][0] >> 16);
-        hi[0] = e4m3x2_to_h2bits(sc[j][1]);
-        hi[1] = e4m3x2_to_h2bits(sc[j][1] >> 16);
-        *reinterpret_cast<u32x2_t*>(scale_lds + row * SCALE_STRIDE) = lo;
-        *reinterpret_cast<u32x2_t*>(scale_lds + row * SCALE_STRIDE + 8) = hi;
+    for (int j = 0; j < T::B_CPT; ++j) {
+      const int c = t + T::THREADS * j;
+      if ((T::BN * 4) % T::THREADS == 0 || c < T::BN * 4)
+        *reinterpret_cast<u32x4_t*>(codes_lds + (T::BM + (c >> 2)) * CODE_STRIDE + 16 * (c & 3)) = b_codes[j];
+    }
+#pragma unroll
+    for (int j = 0; j < T::SA_PT; ++j) {
+      const int i = t + T::THREADS * j;
+      if ((2 * T::BM) % T::THREADS == 0 || i < 2 * T::BM) {
+        const int g = i / (T::BM / 4), r = 4 * (i % (T::BM / 4));
+        *reinterpret_cast<u32x2_t*>(scale_lds + 2 * (g * T::ROWS + r)) =
+            u32x2_t{e4m3x2_to_h2bits(a_sc[j]), e4m3x2_to_h2bits(a_sc[j] >> 16)};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < T::SB_PT; ++j) {
+      const int i = t + T::THREADS * j;
+      if ((2 * T::BN) % T::THREADS == 0 || i < 2 * T::BN) {
+        const int g = i / (T::BN / 4), r = T::BM + 4 * (i % (T::BN / 4));
+        *reinterpret_cast<u32x2_t*>(scale_lds + 2 * (g * T::ROWS + r)) =
+            u32x2_t{e4m3x2_to_h2bits(b_sc[j]), e4m3x2_to_h2bits(b_sc[j] >> 16)};
       }
     }
   }
 };
 
-template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16, int RB>
+// Two float32 -> packed bf16 pair, round to nearest even (hardware convert).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = __builtin_convertvector(float2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// The MFMA's first operand carries weight rows (output columns n) and its second operand
+// activation rows (output rows m): each lane's accumulator then holds 4 consecutive n of
+// one m per register quad, which is stored directly as 8 contiguous bytes of y.
+template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16, bool LORA, bool SC4>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
@@ -157,6 +235,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   const int kbytes = K / 2;
   const int groups = K / 16;
   const int nkt = (K + BK - 1) / BK;
+  const int nfull = kbytes / (BK / 2);  // K-steps with no column past K
 
   float16_t acc[FM][FN];
 #pragma unroll
@@ -167,57 +246,74 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   Stager<T, VEC16> st;
-  st.load(qa, qw, sa, sw, M, N, m0, n0, 0, kbytes, groups, t);
+  const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);
+  st.init(rows_a, rows_b, M, N, kbytes, t);
+  if (0 < nfull) st.template load<false, SC4>(qa, qw, sa, sw, M, N, m0, n0, rows_a, rows_b, 0, kbytes, groups, t);
+  else st.template load<true, SC4>(qa, qw, sa, sw, M, N, m0, n0, rows_a, rows_b, 0, kbytes, groups, t);
   st.store(lds, t);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const bool more = kt + 1 < nkt;
-    if (more) st.load(qa, qw, sa, sw, M, N, m0, n0, kt + 1, kbytes, groups, t);
+    if (more) {
+      if (kt + 1 < nfull)
+        st.template load<false, SC4>(qa, qw, sa, sw, M, N, m0, n0, rows_a, rows_b, kt + 1, kbytes, groups, t);
+      else
+        st.template load<true, SC4>(qa, qw, sa, sw, M, N, m0, n0, rows_a, rows_b, kt + 1, kbytes, groups, t);
+    }
     const uint8_t* cur = lds + (kt & 1) * T::STAGE_BYTES;
     const uint8_t* codes_lds = cur;
     const uint8_t* scale_lds = cur + T::ROWS * CODE_STRIDE;
 
-    // scales for this stage: groups 4h .. 4h+3 of each fragment row, as f16
+    // This stage's operands for the wave: scales of groups 4h .. 4h+3 of each fragment row
+    // (f16, packed in pairs) and both halves of the packed codes.
     uint32_t sA[FM][2], sB[FN][2];
+    u32x4_t cA[2][FM], cB[2][FN];
+    const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(scale_lds);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm * FM * 32 + i * 32 + l32;
-      u32x2_t v = *reinterpret_cast<const u32x2_t*>(scale_lds + row * SCALE_STRIDE + 8 * h);
-      sA[i][0] = v[0]; sA[i][1] = v[1];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        sA[i][p] = (uint32_t)sc16[(4 * h + 2 * p) * T::ROWS + row] | ((uint32_t)sc16[(4 * h + 2 * p + 1) * T::ROWS + row] << 16);
+      cA[0][i] = *reinterpret_cast<const u32x4_t*>(codes_lds + row * CODE_STRIDE + 32 * h);
+      cA[1][i] = *reinterpret_cast<const u32x4_t*>(codes_lds + row * CODE_STRIDE + 32 * h + 16);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = T::BM + wn * FN * 32 + j * 32 + l32;
-      u32x2_t v = *reinterpret_cast<const u32x2_t*>(scale_lds + row * SCALE_STRIDE + 8 * h);
-      sB[j][0] = v[0]; sB[j][1] = v[1];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        sB[j][p] = (uint32_t)sc16[(4 * h + 2 * p) * T::ROWS + row] | ((uint32_t)sc16[(4 * h + 2 * p + 1) * T::ROWS + row] << 16);
+      cB[0][j] = *reinterpret_cast<const u32x4_t*>(codes_lds + row * CODE_STRIDE + 32 * h);
+      cB[1][j] = *reinterpret_cast<const u32x4_t*>(codes_lds + row * CODE_STRIDE + 32 * h + 16);
     }
+    // Software pipeline over the 8 sub-steps: sub-step kk + 1 is decoded while the MFMAs of
+    // sub-step kk run.
+    half8_t av[FM], bv[FN];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4_t cA[FM], cB[FN];
+    for (int i = 0; i < FM; ++i) av[i] = decode8(cA[0][i][0], scale_pair(sA[i][0], 0));
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * FM * 32 + i * 32 + l32;
-        cA[i] = *reinterpret_cast<const u32x4_t*>(codes_lds + row * CODE_STRIDE + 32 * h + 16 * half);
+    for (int j = 0; j < FN; ++j) bv[j] = decode8(cB[0][j][0], scale_pair(sB[j][0], 0));
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      half8_t an[FM], bn[FN];
+      if (kk < 7) {
+        const int k1 = kk + 1, hf = k1 >> 2, q = k1 & 3, g = k1 >> 1;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) an[i] = decode8(cA[hf][i][q], scale_pair(sA[i][g >> 1], g & 1));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bn[j] = decode8(cB[hf][j][q], scale_pair(sB[j][g >> 1], g & 1));
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = T::BM + wn * FN * 32 + j * 32 + l32;
-        cB[j] = *reinterpret_cast<const u32x4_t*>(codes_lds + row * CODE_STRIDE + 32 * h + 16 * half);
-      }
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kk = 4 * half + q;  // group within the lane's half: kk / 2
-        const int g = kk >> 1;
-        half8_t av[FM], bv[FN];
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[i][j], 0, 0, 0);
+      if (kk < 7) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) av[i] = decode8(cA[i][q], scale_pair(sA[i][g >> 1], g & 1));
+        for (int i = 0; i < FM; ++i) av[i] = an[i];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bv[j] = decode8(cB[j][q], scale_pair(sB[j][g >> 1], g & 1));
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) bv[j] = bn[j];
       }
     }
     if (more) st.store(lds + ((kt + 1) & 1) * T::STAGE_BYTES, t);
@@ -225,25 +321,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   }
 
   // ---- epilogue -------------------------------------------------------------------------
-  // All loads below read clamped, valid addresses and zero out-of-range values (branch-free).
+  // acc[i][j][4q + e] is y[m, n] with m = mb + i*32 + l32, n = nb + j*32 + 8q + 4h + e.
+  const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
   const float ts = bf16_bits_to_f32(wts[0]);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * FN * 32 + j * 32 + l32;
-    const float c = bf16_bits_to_f32(wcs[n < N ? n : 0]) * ts;
-    const float cs = n < N ? c : 0.0f;
+  for (int j = 0; j < FN; ++j)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] *= cs;
-  }
-  if (RB > 0) {
+      for (int e = 0; e < 4; ++e) {
+        const int n = nb + j * 32 + 8 * q + 4 * h + e;
+        const float c = n < N ? bf16_bits_to_f32(wcs[n < N ? n : 0]) * ts : 0.0f;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+        for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c;
+      }
+    }
+  if (LORA) {
+    const int nrb = (R + 15) / 16;
+    for (int rb = 0; rb < nrb; ++rb) {
       bf16x8_t pv[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * FN * 32 + j * 32 + l32;
+        const int n = nb + j * 32 + l32;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = rb * 16 + 8 * h + e;
@@ -254,7 +353,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * FM * 32 + i * 32 + l32;
+        const int m = mb + i * 32 + l32;
         bf16x8_t lhi, llo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -268,40 +367,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lhi, pv[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(llo, pv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], llo, acc[i][j], 0, 0, 0);
         }
       }
     }
   }
-  // bf16 tile -> LDS (row-major BM x BN), then 16-byte row-contiguous global stores.
-  uint16_t* out_lds = reinterpret_cast<uint16_t*>(lds);
+  const bool n4 = (N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int m = mb + i * 32 + l32;
+    if (m >= M) continue;
+    uint16_t* yrow = y + (size_t)m * N;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = wn * FN * 32 + j * 32 + l32;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * FM * 32 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        out_lds[row * T::BN + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb + j * 32 + 8 * q + 4 * h;
+        const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        if (n4) {
+          if (n < N) *reinterpret_cast<u32x2_t*>(yrow + n) = u32x2_t{p0, p1};
+        } else {
+          const uint16_t v[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) yrow[n + e] = v[e];
+        }
       }
-    }
-  __syncthreads();
-  constexpr int VEC_PER_ROW = T::BN / 8;  // 8 bf16 per 16-byte store
-  const bool n_vec = (N % 8) == 0;
-  for (int v = t; v < T::BM * VEC_PER_ROW; v += T::THREADS) {
-    const int row = v / VEC_PER_ROW, cv = v % VEC_PER_ROW;
-    const int m = m0 + row, n = n0 + cv * 8;
-    if (m >= M || n >= N) continue;
-    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(out_lds + row * T::BN + cv * 8);
-    uint16_t* dst = y + (size_t)m * N + n;
-    if (n_vec && n + 8 <= N && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
-      *reinterpret_cast<u32x4_t*>(dst) = val;
-    } else {
-      const uint16_t* s16 = out_lds + row * T::BN + cv * 8;
-      for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = s16[e];
-    }
   }
 }
 
@@ -312,17 +405,16 @@ hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* s
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
   dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
   dim3 block(T::THREADS);
-#define W4A4_GEMM_LAUNCH(RBV)                                                                      \
-  gemm_kernel<WAVES_M, WAVES_N, FM, FN, VEC16, RBV><<<grid, block, 0, st>>>(qa, sa, lora, qw, sw, pu, wcs, \
-                                                                            wts, M, N, K, R, y)
-  switch (rb) {
-    case 0: W4A4_GEMM_LAUNCH(0); break;
-    case 1: W4A4_GEMM_LAUNCH(1); break;
-    case 2: W4A4_GEMM_LAUNCH(2); break;
-    case 3: W4A4_GEMM_LAUNCH(3); break;
-    default: W4A4_GEMM_LAUNCH(4); break;
+  const bool sc4 = (M % 4) == 0 && (N % 4) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sw)) & 3) == 0;
+#define W4A4_GEMM_GO(L, S) \
+  gemm_kernel<WAVES_M, WAVES_N, FM, FN, VEC16, L, S><<<grid, block, 0, st>>>(qa, sa, lora, qw, sw, pu, wcs, wts, M, N, K, R, y)
+  if (rb > 0) {
+    if (sc4) W4A4_GEMM_GO(true, true); else W4A4_GEMM_GO(true, false);
+  } else {
+    if (sc4) W4A4_GEMM_GO(false, true); else W4A4_GEMM_GO(false, false);
   }
-#undef W4A4_GEMM_LAUNCH
+#undef W4A4_GEMM_GO
   return hipGetLastError();
 }
 
@@ -334,16 +426,24 @@ hipError_t launch_tile(int rb, bool vec16, hipStream_t st, const uint8_t* qa, co
   return launch_rb<WAVES_M, WAVES_N, FM, FN, false>(rb, st, qa, sa, lora, qw, sw, pu, wcs, wts, M, N, K, R, y);
 }
 
-// Number of workgroups that fill the chip in whole waves of 256 CUs, scored so that
-// larger tiles win when the fill is equal.
+// Score of a tile shape for an M x N problem: fill of whole waves of 256 CUs times the useful
+// fraction of the padded tiles; larger tiles win ties (less staging per MFMA).
 double tile_score(int64_t M, int64_t N, int bm, int bn) {
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t rounds = (tiles + 255) / 256;
   const double fill = (double)tiles / (double)(rounds * 256);
   const double useful = (double)(M * N) / (double)(((M + bm - 1) / bm) * bm * ((N + bn - 1) / bn) * bn);
-  const double per_mfma_decode = (double)(bm / 64 + bn / 64) / (double)((bm / 64) * (bn / 64));  // lower is better
-  return fill * useful / (1.0 + 0.5 * per_mfma_decode);
+  return fill * useful * (1.0 + 1e-3 * (double)(bm * bn) / 65536.0);
 }
+
+struct Variant {
+  const char* name;  // waves_m x waves_n x fm x fn
+  int wm, wn, fm, fn;
+};
+constexpr Variant kVariants[] = {
+    {"2x2x4x4", 2, 2, 4, 4}, {"2x2x4x3", 2, 2, 4, 3}, {"2x2x4x2", 2, 2, 4, 2}, {"2x2x2x2", 2, 2, 2, 2},
+    {"4x2x2x4", 4, 2, 2, 4}, {"2x4x4x2", 2, 4, 4, 2}, {"4x2x2x3", 4, 2, 2, 3},
+};
 
 }  // namespace
 
@@ -361,20 +461,33 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
   auto wt = static_cast<const uint16_t*>(wtscale);
   auto yp = static_cast<uint16_t*>(y);
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R;
-  // candidate tiles (BM x BN): 256x256, 256x192, 256x128, 128x128; W4A4_GEMM_TILE forces one
-  double s256 = tile_score(M, N, 256, 256), s192 = tile_score(M, N, 256, 192);
-  double s128 = tile_score(M, N, 256, 128), s64 = tile_score(M, N, 128, 128);
-  static const char* forced = getenv("W4A4_GEMM_TILE");
-  if (forced) {
-    const bool a = !strcmp(forced, "256x256"), b = !strcmp(forced, "256x192"), c = !strcmp(forced, "256x128"),
-               d = !strcmp(forced, "128x128");
-    if (a || b || c || d) { s256 = a; s192 = b; s128 = c; s64 = d; }
+  // Pick the best-scoring variant; W4A4_GEMM_TILE (a variant name) forces one.
+  const char* forced = getenv("W4A4_GEMM_TILE");
+  int best = -1;
+  double best_score = -1.0;
+  for (int i = 0; i < (int)(sizeof(kVariants) / sizeof(kVariants[0])); ++i) {
+    const Variant& v = kVariants[i];
+    // automatic choice: the 8-wave layouts (two waves per SIMD hide each other's LDS and
+    // barrier waits) and the small 4-wave 128 x 128 tile
+    if (strcmp(v.name, "2x4x4x2") && strcmp(v.name, "4x2x2x3") && strcmp(v.name, "2x2x2x2")) continue;
+    const double sc = tile_score(M, N, v.wm * v.fm * 32, v.wn * v.fn * 32);
+    if (sc > best_score) { best_score = sc; best = i; }
   }
-  const double best = fmax(fmax(s256, s192), fmax(s128, s64));
-  if (best == s256) return launch_tile<2, 2, 4, 4>(rb, vec16, stream, qa, sa, lora, qw, sw, pu, wc, wt, m, n, k, r, yp);
-  if (best == s192) return launch_tile<2, 2, 4, 3>(rb, vec16, stream, qa, sa, lora, qw, sw, pu, wc, wt, m, n, k, r, yp);
-  if (best == s128) return launch_tile<2, 2, 4, 2>(rb, vec16, stream, qa, sa, lora, qw, sw, pu, wc, wt, m, n, k, r, yp);
-  return launch_tile<2, 2, 2, 2>(rb, vec16, stream, qa, sa, lora, qw, sw, pu, wc, wt, m, n, k, r, yp);
+  if (forced)
+    for (int i = 0; i < (int)(sizeof(kVariants) / sizeof(kVariants[0])); ++i)
+      if (!strcmp(forced, kVariants[i].name)) best = i;
+#define W4A4_TILE_CASE(I, WM, WN, FM, FN) \
+  case I: return launch_tile<WM, WN, FM, FN>(rb, vec16, stream, qa, sa, lora, qw, sw, pu, wc, wt, m, n, k, r, yp);
+  switch (best) {
+    W4A4_TILE_CASE(0, 2, 2, 4, 4)
+    W4A4_TILE_CASE(1, 2, 2, 4, 3)
+    W4A4_TILE_CASE(2, 2, 2, 4, 2)
+    W4A4_TILE_CASE(3, 2, 2, 2, 2)
+    W4A4_TILE_CASE(4, 4, 2, 2, 4)
+    W4A4_TILE_CASE(5, 2, 4, 4, 2)
+    default: return launch_tile<4, 2, 2, 3>(rb, vec16, stream, qa, sa, lora, qw, sw, pu, wc, wt, m, n, k, r, yp);
+  }
+#undef W4A4_TILE_CASE
 }
 
 }  // namespace w4a4

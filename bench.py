@@ -52,6 +52,7 @@ def sha_of(paths):
 
 KERNEL_SOURCES = {
     "gemm": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
+    "gemm_skinny": ["w4a4_bit_quantized_amd/csrc/gemm_skinny.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "quantize": ["w4a4_bit_quantized_amd/csrc/quantize.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
 }
 

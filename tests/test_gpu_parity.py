@@ -125,6 +125,12 @@ GEMM_CASES = [
     (128, 128, 128, 32),
     (16, 600, 5120, 32),
     (200, 64, 3072, 1),
+    # batches of at most 32 rows take the weight-streaming kernel
+    (5, 300, 640, 8),
+    (17, 100, 3072, 32),
+    (32, 129, 48, 5),
+    (31, 64, 4096, 64),
+    (2, 33, 16, 0),
 ]
 
 
@@ -146,7 +152,9 @@ def test_gemm_every_tile_variant(w4, variant, monkeypatch):
 
 
 @pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 0), (37, 70, 256, 32, 128), (3, 40, 48, 3, 16),
-                                       (150, 260, 512, 64, 64)])
+                                       (150, 260, 512, 64, 64),
+                                       # small batches: K split across quantizer workgroups (partial low-rank sums)
+                                       (16, 200, 4096, 32, 0), (9, 100, 8192, 16, 128), (32, 64, 1024, 64, 32)])
 def test_linear_parity(w4, M, N, K, R, B):
     import torch
     lay = synth.make_layer("tiny", seed=11 + M, M=M, K=K, N=N, R=R, B=B, wcs="uniform")

@@ -79,7 +79,7 @@ w4a4_status svdq_quantize_act(const void* x, const void* smooth_factor, const vo
   w4a4_status st = validate_quantize_act(x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales, lora_act);
   if (st != W4A4_OK || M == 0) return st;
   (void)hipGetLastError();  // clear a stale error so it is not reported as ours
-  return from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales,
+  return from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, 1, qact, ascales,
                                         lora_act, static_cast<hipStream_t>(stream)));
 }
 
@@ -92,8 +92,8 @@ w4a4_status svdq_quantize_weight(const void* w, const void* smooth_factor, int64
   if (!w || !smooth_factor || !qweight || !wscales) return W4A4_ERR_NULL;
   if (!aligned(w, 16) || !aligned(smooth_factor, 16) || !aligned(qweight, 4)) return W4A4_ERR_ALIGN;
   (void)hipGetLastError();
-  return from_hip(w4a4::launch_quantize(false, w, smooth_factor, nullptr, N, K, 0, hadamard_block, qweight, wscales,
-                                        nullptr, static_cast<hipStream_t>(stream)));
+  return from_hip(w4a4::launch_quantize(false, w, smooth_factor, nullptr, N, K, 0, hadamard_block, 1, qweight,
+                                        wscales, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 w4a4_status svdq_gemm_lowrank(const void* qact, const void* ascales, const float* lora_act, const void* qweight,
@@ -102,14 +102,15 @@ w4a4_status svdq_gemm_lowrank(const void* qact, const void* ascales, const float
   w4a4_status st = validate_gemm(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
   if (st != W4A4_OK || M == 0 || N == 0) return st;
   (void)hipGetLastError();
-  return from_hip(w4a4::launch_gemm(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, M, N, K,
-                                    R, y, static_cast<hipStream_t>(stream)));
+  return from_hip(w4a4::launch_gemm(qact, ascales, lora_act, 1, qweight, wscales, proj_up, wcscales, wtscale, M, N,
+                                    K, R, y, static_cast<hipStream_t>(stream)));
 }
 
 size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int64_t R) {
   if (M < 0 || M > kMaxDim || check_k_rank_block(K, R, 0) != W4A4_OK) return 0;
   const size_t m = (size_t)M, k = (size_t)K, r = (size_t)R;
-  return align256(m * k / 2) + align256(k / 16 * m) + align256(m * r * sizeof(float));
+  const size_t parts = (size_t)w4a4::quantize_parts(M, K);
+  return align256(m * k / 2) + align256(k / 16 * m) + align256(parts * m * r * sizeof(float));
 }
 
 w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales, const void* proj_down,
@@ -137,9 +138,12 @@ w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales,
   if (st != W4A4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  st = from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales, lora, s));
+  const int parts = w4a4::quantize_parts(M, K);
+  st = from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, parts, qact, ascales,
+                                      lora, s));
   if (st != W4A4_OK) return st;
-  return from_hip(w4a4::launch_gemm(qact, ascales, lora, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y, s));
+  return from_hip(w4a4::launch_gemm(qact, ascales, lora, parts, qweight, wscales, proj_up, wcscales, wtscale, M, N, K,
+                                    R, y, s));
 }
 
 }  // extern "C"

@@ -217,7 +217,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // one m per register quad, which is stored directly as 8 contiguous bytes of y.
 template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16, bool LORA, bool SC4>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
-    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora,
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
     const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
     uint16_t* __restrict__ y) {
@@ -359,7 +359,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
         for (int e = 0; e < 8; ++e) {
           const int r = rb * 16 + 8 * h + e;
           const bool ok = m < M && r < R;
-          const float f0 = lora[ok ? (size_t)m * R + r : 0];
+          float f0 = 0.0f;
+          for (int p = 0; p < parts; ++p) f0 += lora[ok ? (size_t)p * M * R + (size_t)m * R + r : 0];
           const float f = ok ? f0 : 0.0f;
           const uint32_t hb = f32_to_bf16_bits(f);
           lhi[e] = bf16_from_bits(hb);
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 }
 
 template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16>
-hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora,
+hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                      const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
                      const uint16_t* wts, int M, int N, int K, int R, uint16_t* y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
@@ -408,7 +409,7 @@ hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* s
   const bool sc4 = (M % 4) == 0 && (N % 4) == 0 &&
                    ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sw)) & 3) == 0;
 #define W4A4_GEMM_GO(L, S) \
-  gemm_kernel<WAVES_M, WAVES_N, FM, FN, VEC16, L, S><<<grid, block, 0, st>>>(qa, sa, lora, qw, sw, pu, wcs, wts, M, N, K, R, y)
+  gemm_kernel<WAVES_M, WAVES_N, FM, FN, VEC16, L, S><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y)
   if (rb > 0) {
     if (sc4) W4A4_GEMM_GO(true, true); else W4A4_GEMM_GO(true, false);
   } else {
@@ -420,10 +421,11 @@ hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* s
 
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 hipError_t launch_tile(int rb, bool vec16, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora,
-                       const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
+                       int parts, const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
                        const uint16_t* wts, int M, int N, int K, int R, uint16_t* y) {
-  if (vec16) return launch_rb<WAVES_M, WAVES_N, FM, FN, true>(rb, st, qa, sa, lora, qw, sw, pu, wcs, wts, M, N, K, R, y);
-  return launch_rb<WAVES_M, WAVES_N, FM, FN, false>(rb, st, qa, sa, lora, qw, sw, pu, wcs, wts, M, N, K, R, y);
+  if (vec16)
+    return launch_rb<WAVES_M, WAVES_N, FM, FN, true>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+  return launch_rb<WAVES_M, WAVES_N, FM, FN, false>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
 }
 
 // Score of a tile shape for an M x N problem: fill of whole waves of 256 CUs times the useful
@@ -447,9 +449,12 @@ constexpr Variant kVariants[] = {
 
 }  // namespace
 
-hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora, const void* qweight,
-                       const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
-                       int64_t M, int64_t N, int64_t K, int64_t R, void* y, hipStream_t stream) {
+hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora, int lora_parts,
+                       const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
+                       const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, void* y, hipStream_t stream) {
+  if (M <= SKINNY_MAX_M && !getenv("W4A4_GEMM_TILE"))
+    return launch_gemm_skinny(qact, ascales, lora, lora_parts, qweight, wscales, proj_up, wcscales, wtscale, M, N, K,
+                              R, y, stream);
   const int rb = (int)((R + 15) / 16);
   const bool vec16 = (K % 32) == 0;
   auto qa = static_cast<const uint8_t*>(qact);
@@ -477,7 +482,7 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
     for (int i = 0; i < (int)(sizeof(kVariants) / sizeof(kVariants[0])); ++i)
       if (!strcmp(forced, kVariants[i].name)) best = i;
 #define W4A4_TILE_CASE(I, WM, WN, FM, FN) \
-  case I: return launch_tile<WM, WN, FM, FN>(rb, vec16, stream, qa, sa, lora, qw, sw, pu, wc, wt, m, n, k, r, yp);
+  case I: return launch_tile<WM, WN, FM, FN>(rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
   switch (best) {
     W4A4_TILE_CASE(0, 2, 2, 4, 4)
     W4A4_TILE_CASE(1, 2, 2, 4, 3)
@@ -485,7 +490,8 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
     W4A4_TILE_CASE(3, 2, 2, 2, 2)
     W4A4_TILE_CASE(4, 4, 2, 2, 4)
     W4A4_TILE_CASE(5, 2, 4, 4, 2)
-    default: return launch_tile<4, 2, 2, 3>(rb, vec16, stream, qa, sa, lora, qw, sw, pu, wc, wt, m, n, k, r, yp);
+    default:
+      return launch_tile<4, 2, 2, 3>(rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
   }
 #undef W4A4_TILE_CASE
 }

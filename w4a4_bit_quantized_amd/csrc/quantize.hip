@@ -153,8 +153,14 @@ __global__ __launch_bounds__(1024) void quantize_kernel(
 #pragma unroll
   for (int rb = 0; rb < (RB > 0 ? RB : 1); ++rb) acc[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int u_begin = wave * units_per_wave;
-  const int u_end = min(u_begin + units_per_wave, nunits);
+  // blockIdx.y selects a contiguous part of the units (K split across workgroups for small M;
+  // each part writes its own low-rank partial sum at lora + part * M * R)
+  const int parts = gridDim.y;
+  const int per_part = (nunits + parts - 1) / parts;
+  const int p_begin = blockIdx.y * per_part;
+  const int p_end = min(p_begin + per_part, nunits);
+  const int u_begin = p_begin + wave * units_per_wave;
+  const int u_end = min(u_begin + units_per_wave, p_end);
   for (int u = u_begin; u < u_end; ++u) {
     float v[S][8];
 #pragma unroll
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(1024) void quantize_kernel(
       float sum = 0.0f;
       for (int w = 0; w < nwaves; ++w) sum += red_lds[w * QROWS * RP + rr * RP + cc];
       const int mm = blockIdx.x * QROWS + rr;
-      if (mm < M) lora[(size_t)mm * R + cc] = sum;
+      if (mm < M) lora[(size_t)blockIdx.y * M * R + (size_t)mm * R + cc] = sum;
     }
   }
 }
@@ -277,15 +283,24 @@ hipError_t launch_hb(int hb, int rb, dim3 grid, dim3 block, hipStream_t st, cons
 
 }  // namespace
 
+int quantize_parts(int64_t M, int64_t K) {
+  // Small batches split K across workgroups so that enough CUs stream x; the partial
+  // low-rank sums are added in a fixed order by the consumer.
+  const int64_t n32 = K / 32;
+  if (M > SKINNY_MAX_M || n32 < 32) return 1;
+  return (int)(n32 / 16 < 8 ? n32 / 16 : 8);
+}
+
 hipError_t launch_quantize(bool act, const void* x, const void* lam, const void* pd, int64_t M, int64_t K,
-                           int64_t R, int hb, void* q, void* scales, float* lora, hipStream_t stream) {
+                           int64_t R, int hb, int parts, void* q, void* scales, float* lora, hipStream_t stream) {
   const int cols = hb > 32 ? hb : 32;
   const int nunits = (int)((K + cols - 1) / cols);
-  int nwaves = nunits < QMAX_WAVES ? nunits : QMAX_WAVES;
-  const int upw = (nunits + nwaves - 1) / nwaves;
-  nwaves = (nunits + upw - 1) / upw;
+  const int per_part = (nunits + parts - 1) / parts;
+  int nwaves = per_part < QMAX_WAVES ? per_part : QMAX_WAVES;
+  const int upw = (per_part + nwaves - 1) / nwaves;
+  nwaves = (per_part + upw - 1) / upw;
   const int rb = act ? (int)((R + 15) / 16) : 0;
-  dim3 grid((unsigned)((M + QROWS - 1) / QROWS));
+  dim3 grid((unsigned)((M + QROWS - 1) / QROWS), (unsigned)parts);
   dim3 block((unsigned)(64 * nwaves));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* lp = static_cast<const uint16_t*>(lam);

@@ -58,16 +58,20 @@ KERNEL_SOURCES = {
 
 
 def traffic_from_profile(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, or None if stale/missing."""
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None if stale/missing.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by the factor the same counter
+    gives for a device copy of known size."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
     ent = data.get(f"{kernel}:{workload}")
-    if not ent or ent.get("source_sha") != sha_of(KERNEL_SOURCES[kernel]):
+    cal = data.get("calibration")
+    if not ent or not cal or ent.get("source_sha") != sha_of(KERNEL_SOURCES[kernel]):
         return None
-    return (ent["fetch_kib"] + ent["write_kib"]) * 1024.0 * ent["factor"]
+    return 1024.0 * (ent["fetch_kib"] * cal["fetch_factor"] + ent["write_kib"] * cal["write_factor"])
 
 
 def cpu_baseline(spec_name, cpu_rows, seconds):
@@ -100,6 +104,17 @@ def cpu_baseline(spec_name, cpu_rows, seconds):
             "sample": f"{rows} of {lay['M']} rows of {spec_name} (K={lay['K']}, N={lay['N']}, R={lay['R']}), "
                       f"whole layer (smooth, rotate, quantize, dequantize, float64 GEMM, epilogue), "
                       f"mean of {reps} runs, {t:.3f} s each; weight quantization untimed"}
+
+
+def sleep_cycles(torch, stream, seconds):
+    """Argument for torch.cuda._sleep that spins the GPU for about `seconds` (its clock, measured)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_cycle = max(e0.elapsed_time(e1) * 1e-3, 1e-6) / (1 << 20)
+    return int(min(seconds / per_cycle, 1 << 31))
 
 
 def main():
@@ -207,6 +222,9 @@ def main():
     # per-kernel durations: the same two kernels through the two-entry-point form, HIP events between them
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # a bounded spin kernel first, so that the host queues the whole loop before the GPU reaches it and
+    # no event pair spans a launch gap
+    torch.cuda._sleep(sleep_cycles(torch, stream, 2e-3 + 40e-6 * args.steps))
     for i in range(args.steps):
         e0, e1, e2 = evs[i]
         e0.record(stream)
@@ -245,7 +263,9 @@ def main():
         ach = g_bytes / (g_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": "gemm_lowrank"}
-    tr = traffic_from_profile("gemm", args.workload)
+    gemm_kernel = "gemm_skinny" if M <= 32 else "gemm"
+    roof["kernel"] = gemm_kernel
+    tr = traffic_from_profile(gemm_kernel, args.workload)
     roof["traffic"] = None if tr is None else round(tr)
 
     cpu = None

@@ -225,6 +225,25 @@ def test_special_values(w4):
     _check_quant_act(w4, lay)
 
 
+@pytest.mark.parametrize("B", [0, 128])
+def test_smoothing_outside_fast_range(w4, B):
+    """Smoothing factors and activations outside the range where the kernel's reciprocal-based
+    division is exact (huge, tiny and negative smoothing factors, huge and tiny activations):
+    the IEEE path must give the same bit-exact codes and scales."""
+    lay = synth.make_layer("tiny", seed=11 + B, M=40, K=512, N=8, R=16, B=B)
+    lam = synth.bits_to_f32(lay["smooth_factor"]).copy()
+    lam[3] = np.float32(2.0 ** 40)
+    lam[130] = np.float32(2.0 ** -40)
+    lam[300] = np.float32(-1.5)
+    lay["smooth_factor"] = synth.to_bf16_bits(lam)
+    x = synth.bits_to_f32(lay["x"]).copy()
+    x[5, 200] = np.float32(1e35)
+    x[6, 7] = np.float32(-3e-30)
+    x[7, 400:416] = -0.0
+    lay["x"] = synth.to_bf16_bits(x)
+    _check_quant_act(w4, lay)
+
+
 def test_deterministic(w4):
     import torch
     lay = synth.make_layer("tiny", seed=9, M=300, K=1024, N=520, R=32)

@@ -9,17 +9,39 @@
 //   s8  = e4m3(f32(amax|v| / 6)),  code = e2m1(f32(v / e4m3_value(s8))), 0 when s8 == 0
 //   lora_act = x_s @ proj_down (activations only; unrotated x_s)
 //
-// Work decomposition: one workgroup per 16 rows, its waves splitting K into
-// contiguous chunks of whole "units" (32 columns, or one Hadamard block when
-// B > 32).  Lane l of a wave holds row l % 16 and the 8 consecutive columns
-// 8 * (l / 16) .. +8 of each 32-column step, which is exactly the A-operand
-// layout of the 16x16x32 bf16 MFMA used for the low-rank down-projection.
-// A 16-group spans lanes l and l ^ 16.  Butterfly spans 1..4 stay in a lane,
-// spans 8 and 16 cross lanes (xor 16, xor 32), spans 32 and 64 cross steps.
-// The down-projection runs on the matrix cores with x_s split into a bf16
-// high part and a bf16 low part (x_s = hi + lo to 16 significant bits); the
-// per-wave partial sums are reduced across waves in a fixed order through
-// LDS, so results are deterministic.
+// Work decomposition.  A workgroup owns 16 rows; its waves split K into
+// contiguous runs of units (64 columns, or 128 for B = 128).  A unit is one or
+// two 64-column steps.  In a step, lane l holds row l % 16 and the 16
+// consecutive columns 16 * (l / 16) .. +16: exactly one quantization group, so
+// the group maximum, the scale and the eight code bytes stay inside the lane.
+// Butterfly spans 1..8 are in-lane; spans 16 and 32 pair lane l with l ^ 16 and
+// l ^ 32 (v_permlane16_swap / v_permlane32_swap on pairs of registers: one
+// swap brings both partners' values together, every lane forms a + b and
+// a - b, a second swap returns the results); span 64 joins the two steps of a
+// 128-column unit.
+//
+// Division.  Both divisions are correctly rounded.  x / lambda uses the
+// reciprocal r = RN(1/lambda) (one IEEE division per column, computed once per
+// unit and shared through LDS) and one Markstein correction:
+//   q0 = RN(x r),  e = RN(q0 lambda - x) (exact, fused),  q = RN(q0 - e r).
+// For bf16 x with 2^-64 <= |x| < 2^96 (or x = +-0) and bf16 lambda in
+// [2^-32, 2^32] this equals RN(x / lambda) bit for bit, signed zeros included
+// (checked exhaustively over every such pair of bf16 mantissas and exponent
+// offsets); units or waves whose inputs fall outside that range take the IEEE
+// division instead.  v / sd uses the same sequence with r = RN(1/sd) from a
+// 128-entry table; there the E2M1 code of the result equals the code of the
+// IEEE quotient for every finite v and every nonzero e4m3 sd reachable from the
+// group maximum (checked near every decision point and across all binades);
+// groups whose maximum is not finite take the IEEE division.
+//
+// Low-rank down-projection.  x_s is split into a bf16 high part and a bf16 low
+// part (x_s = hi + lo to about 16 significant bits) that feed the 16x16x32 bf16
+// MFMA as the A operand: lane (row, quarter q) supplies columns 16q .. 16q+8 of
+// its group in one MFMA and 16q+8 .. 16q+16 in the next.  The matching
+// proj_down operand is staged per wave in LDS, row-major as in memory, and read
+// with the transposing ds_read_b64_tr_b16, which hands each lane four
+// consecutive K-rows of one rank column.  Per-wave partial sums are reduced
+// across waves in a fixed order through LDS, so results are deterministic.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,13 +49,27 @@ namespace w4a4 {
 
 namespace {
 
-constexpr int QROWS = 16;        // rows per workgroup
-constexpr int QMAX_WAVES = 16;   // waves per workgroup (split of K)
+constexpr int QROWS = 16;  // rows per workgroup
 
-template <int HB>
-struct Unit {
-  static constexpr int COLS = HB > 32 ? HB : 32;  // columns per unit
-  static constexpr int STEPS = COLS / 32;         // 32-column steps per unit
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int max_waves(int hb, int rb) { return (rb > 2 || (hb == 128 && rb > 0)) ? 8 : 16; }
+
+template <int HB, bool ACT, int RB>
+struct QCfg {
+  static constexpr int UC = HB == 128 ? 128 : 64;  // columns per unit
+  static constexpr int US = UC / 64;               // 64-column steps per unit
+  static constexpr int RP = RB * 16;               // padded rank
+  static constexpr int RS = RP + 16;               // LDS row stride of proj_down (u16), 32 bytes of padding
+  static constexpr int WAVES = max_waves(HB, RB);  // most waves per workgroup (register budget)
+  static constexpr int PD_BYTES = (ACT && RB > 0) ? 64 * RS * 2 : 0;
+  static constexpr int LAM_BYTES = ACT ? 2 * UC * 4 : 0;
+  static constexpr int WAVE_BYTES = PD_BYTES + LAM_BYTES;
+  static constexpr int RED_BYTES = (ACT && RB > 0) ? WAVES * QROWS * RP * 4 : 0;
+  static constexpr int BODY_BYTES = WAVES * WAVE_BYTES > RED_BYTES ? WAVES * WAVE_BYTES : RED_BYTES;
+  static constexpr int LDS_BYTES = 512 + BODY_BYTES;  // 128-entry reciprocal table first
 };
 
 template <int HB>
@@ -44,114 +80,164 @@ __device__ __forceinline__ float hadamard_scale() {
   return __uint_as_float(0x3DB504F3u);                 // RN(1/sqrt(128))
 }
 
-// Butterfly stage across lanes: partner = lane ^ mask.  The lane whose
-// column is lower keeps a + b, the upper one a - b (a = lower value).
-__device__ __forceinline__ float xlane_butterfly(float mine, int mask, bool lower) {
-  float other = __shfl_xor(mine, mask, 64);
-  return lower ? (mine + other) : (other - mine);
+// Butterfly between lanes l and l ^ 16 (SWAP32 = false) or l ^ 32 (true) on two
+// registers at once.  The lane with the lower column keeps a + b, the other a - b.
+template <bool SWAP32>
+__device__ __forceinline__ void xlane_pair(float& a, float& b) {
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  uint32_t p0, p1;
+  if (SWAP32) {
+    auto s = __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+    p0 = s[0]; p1 = s[1];
+  } else {
+    auto s = __builtin_amdgcn_permlane16_swap(ua, ub, false, false);
+    p0 = s[0]; p1 = s[1];
+  }
+  // lower lane now holds (a_low, a_high), upper lane (b_low, b_high)
+  const float lo = __uint_as_float(p0), hi = __uint_as_float(p1);
+  const float sum = lo + hi, dif = lo - hi;
+  uint32_t r0, r1;
+  if (SWAP32) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(dif), false, false);
+    r0 = s[0]; r1 = s[1];
+  } else {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum), __float_as_uint(dif), false, false);
+    r0 = s[0]; r1 = s[1];
+  }
+  a = __uint_as_float(r0);
+  b = __uint_as_float(r1);
 }
 
-template <int HB, int S>
-__device__ __forceinline__ void fwht_unit(float (&v)[S][8], int oct) {
-  // spans 1, 2, 4: inside the lane's 8 consecutive columns
+template <int HB, int US>
+__device__ __forceinline__ void fwht_unit(float (&v)[US][16]) {
+  // spans 1, 2, 4, 8: inside the lane's 16 consecutive columns
 #pragma unroll
-  for (int h = 1; h < 8 && h < HB; h *= 2) {
+  for (int h = 1; h < 16 && h < HB; h *= 2)
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+    for (int c = 0; c < US; ++c)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 16; ++i)
         if ((i & h) == 0) {
-          float a = v[s][i], b = v[s][i + h];
-          v[s][i] = a + b;
-          v[s][i + h] = a - b;
+          const float a = v[c][i], b = v[c][i + h];
+          v[c][i] = a + b;
+          v[c][i + h] = a - b;
         }
-      }
+  if (HB >= 32)  // span 16: lanes l and l ^ 16
+#pragma unroll
+    for (int c = 0; c < US; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) xlane_pair<false>(v[c][i], v[c][i + 1]);
+  if (HB >= 64)  // span 32: lanes l and l ^ 32
+#pragma unroll
+    for (int c = 0; c < US; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) xlane_pair<true>(v[c][i], v[c][i + 1]);
+  if (HB >= 128)  // span 64: the unit's two steps
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float a = v[0][i], b = v[US - 1][i];
+      v[0][i] = a + b;
+      v[US - 1][i] = a - b;
     }
-  }
-  if (HB >= 16) {  // span 8: octets 2j and 2j+1 -> lanes xor 16
+  const float cb = hadamard_scale<HB>();
 #pragma unroll
-    for (int s = 0; s < S; ++s)
+  for (int c = 0; c < US; ++c)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[s][i] = xlane_butterfly(v[s][i], 16, (oct & 1) == 0);
-  }
-  if (HB >= 32) {  // span 16: octets j and j+2 -> lanes xor 32
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[s][i] = xlane_butterfly(v[s][i], 32, (oct & 2) == 0);
-  }
-  // spans 32, 64: between 32-column steps held by the same lane
-#pragma unroll
-  for (int hs = 1; hs < S; hs *= 2) {
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if ((s & hs) == 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float a = v[s][i], b = v[s + hs][i];
-          v[s][i] = a + b;
-          v[s + hs][i] = a - b;
-        }
-      }
-    }
-  }
-  const float c = hadamard_scale<HB>();
-#pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[s][i] = v[s][i] * c;
+    for (int i = 0; i < 16; ++i) v[c][i] = v[c][i] * cb;
 }
 
-// Quantize the lane's 8 values (half of one 16-group) and store codes/scale.
-__device__ __forceinline__ void quantize_store(const float (&v)[8], bool store, bool store_scale,
-                                               uint8_t* __restrict__ qrow, size_t qoff,
-                                               uint8_t* __restrict__ scale_ptr) {
+// x / d correctly rounded for the operand ranges stated at the top of the file.
+__device__ __forceinline__ float div_markstein(float x, float d, float r) {
+  const float q0 = x * r;
+  const float e = fmaf(q0, d, -x);
+  return fmaf(-e, r, q0);
+}
+
+// Eight float32 -> eight E2M1 codes in one dword (element i in nibble i).
+__device__ __forceinline__ uint32_t pack8(const float (&t)[8]) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[0], t[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[2], t[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[4], t[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[6], t[7], 1.0f, 3);
+}
+
+// Quantize one group (the lane's 16 values): 8 code bytes and the scale byte.
+__device__ __forceinline__ void quantize_group(const float (&v)[16], const float* rtab, u32x2_t& codes,
+                                               uint32_t& s8) {
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const float s = __fdiv_rn(amax, 6.0f);
-  const uint32_t s8 = e4m3_encode_nonneg(s);
+  s8 = e4m3_encode_nonneg(s);
   const float sd = e4m3_decode(s8);
-  uint32_t word = 0u;
-  if (sd != 0.0f) {
+  const float rs = rtab[s8];
+  uint32_t w[2];
+  if (__builtin_amdgcn_ballot_w64(!__builtin_isfinite(amax)) == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float a = __fdiv_rn(v[2 * j], sd);
-      float b = __fdiv_rn(v[2 * j + 1], sd);
-      word |= e2m1_pack2(a, b) << (8 * j);
+    for (int h = 0; h < 2; ++h) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = div_markstein(v[8 * h + i], sd, rs);
+      w[h] = pack8(t);
+    }
+  } else {  // some lane's group holds an infinity: IEEE division for the whole wave
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = __fdiv_rn(v[8 * h + i], sd);
+      w[h] = pack8(t);
     }
   }
-  if (store) *reinterpret_cast<uint32_t*>(qrow + qoff) = word;
-  if (store_scale) *scale_ptr = (uint8_t)s8;
+  const bool nz = sd != 0.0f;
+  codes = u32x2_t{nz ? w[0] : 0u, nz ? w[1] : 0u};
+}
+
+// Raw input check for the fast x / lambda: every bf16 in `d` is +-0 or has
+// 2^-64 <= |x| < 2^96.  Accumulates packed u16 minima / maxima.
+__device__ __forceinline__ void range_acc(uint32_t d, u16x2_t& mn, u16x2_t& mx) {
+  const u16x2_t a = __builtin_bit_cast(u16x2_t, d & 0x7FFF7FFFu);
+  mn = __builtin_elementwise_min(mn, a - (u16x2_t){1, 1});  // +-0 wraps to 0xFFFF
+  mx = __builtin_elementwise_max(mx, a);
+}
+
+__device__ __forceinline__ bool range_bad(u16x2_t mn, u16x2_t mx) {
+  return (mn[0] < 0x1F7Fu) | (mn[1] < 0x1F7Fu) | (mx[0] >= 0x6F80u) | (mx[1] >= 0x6F80u);
 }
 
 template <int HB, bool ACT, int RB>
-__global__ __launch_bounds__(1024) void quantize_kernel(
+__global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam, const uint16_t* __restrict__ pd,
-    int M, int K, int R, int pd_vec, int units_per_wave, int nunits,
+    int M, int K, int R, int units_per_wave, int nunits,
     uint8_t* __restrict__ q, uint8_t* __restrict__ scales, float* __restrict__ lora) {
-  constexpr int COLS = Unit<HB>::COLS;
-  constexpr int S = Unit<HB>::STEPS;
-  constexpr int RP = RB * 16;  // padded rank
-  // LDS: per-wave proj_down staging (32 x RP bf16) and the cross-wave LoRA reduction.
-  __shared__ __attribute__((aligned(16))) uint16_t pd_lds[RB > 0 ? QMAX_WAVES * 32 * RP : 1];
-  __shared__ __attribute__((aligned(16))) float red_lds[RB > 0 ? QMAX_WAVES * QROWS * RP : 1];
+  using C = QCfg<HB, ACT, RB>;
+  constexpr int US = C::US, UC = C::UC, RP = C::RP, RS = C::RS;
+  constexpr bool LORA = ACT && RB > 0;
+  constexpr int PDV = LORA ? RP / 8 : 1;  // 16-byte proj_down chunks per lane per step
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+  float* rtab = reinterpret_cast<float*>(smem);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
   const int row = lane & 15;
-  const int oct = lane >> 4;
-  const int m = blockIdx.x * QROWS + row;
+  const int qd = lane >> 4;
+  const int m0 = blockIdx.x * QROWS;
+  const int m = m0 + row;
   const bool row_ok = m < M;
   const size_t qstride = (size_t)K / 2;
-  uint8_t* qrow = q + (size_t)(row_ok ? m : 0) * qstride;
-  const uint16_t* xrow = x + (size_t)(row_ok ? m : 0) * K;
+  // rows past M read row m0 (valid, finite) and never store
+  const uint16_t* xrow = x + (size_t)(row_ok ? m : m0) * K;
+  uint8_t* qrow = q + (size_t)(row_ok ? m : m0) * qstride;
 
-  float4_t acc[RB > 0 ? RB : 1];
-#pragma unroll
-  for (int rb = 0; rb < (RB > 0 ? RB : 1); ++rb) acc[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint8_t* wbase = smem + 512 + wave * C::WAVE_BYTES;
+  float* lam_s = reinterpret_cast<float*>(wbase + C::PD_BYTES);
+  float* rlam_s = lam_s + UC;
+  uint16_t* pd_s = reinterpret_cast<uint16_t*>(wbase);
+
+  for (int b = threadIdx.x; b < 128; b += blockDim.x)
+    rtab[b] = (b == 0 || b == 127) ? 0.0f : __fdiv_rn(1.0f, e4m3_decode((uint32_t)b));
+  __syncthreads();
 
   // blockIdx.y selects a contiguous part of the units (K split across workgroups for small M;
   // each part writes its own low-rank partial sum at lora + part * M * R)
@@ -161,123 +247,302 @@ __global__ __launch_bounds__(1024) void quantize_kernel(
   const int p_end = min(p_begin + per_part, nunits);
   const int u_begin = p_begin + wave * units_per_wave;
   const int u_end = min(u_begin + units_per_wave, p_end);
-  for (int u = u_begin; u < u_end; ++u) {
-    float v[S][8];
+
+  float4_t acc[RB > 0 ? RB : 1];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int kk = u * COLS + 32 * s + 8 * oct;
-      const bool k_ok = kk < K;
-      u32x4_t xr = {0u, 0u, 0u, 0u};
-      u32x4_t lr = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // 1.0 pairs
-      if (k_ok) {
-        lr = *reinterpret_cast<const u32x4_t*>(lam + kk);
-        if (row_ok) xr = *reinterpret_cast<const u32x4_t*>(xrow + kk);
-      }
+  for (int rb = 0; rb < (RB > 0 ? RB : 1); ++rb) acc[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // ---- loaders ---------------------------------------------------------------------------
+  // x (or w): two 16-byte loads per step; past-K columns read column 0 and are zeroed later.
+  auto load_x = [&](int u, u32x4_t (&dst)[US][2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x0 = __uint_as_float(xr[i] << 16), x1 = __uint_as_float(xr[i] & 0xFFFF0000u);
-        float l0 = __uint_as_float(lr[i] << 16), l1 = __uint_as_float(lr[i] & 0xFFFF0000u);
-        if (ACT) {
-          v[s][2 * i] = __fdiv_rn(x0, l0);
-          v[s][2 * i + 1] = __fdiv_rn(x1, l1);
+    for (int c = 0; c < US; ++c) {
+      const int k0 = u * UC + 64 * c + 16 * qd;
+      const int kk = k0 < K ? k0 : 0;
+      dst[c][0] = *reinterpret_cast<const u32x4_t*>(xrow + kk);
+      dst[c][1] = *reinterpret_cast<const u32x4_t*>(xrow + kk + 8);
+    }
+  };
+  // activations: lambda of column u * UC + 64 c + lane (one per lane); weights: the lane's 16 columns
+  auto load_lam_act = [&](int u, uint32_t (&dst)[US]) {
+#pragma unroll
+    for (int c = 0; c < US; ++c) {
+      const int k = u * UC + 64 * c + lane;
+      dst[c] = k < K ? (uint32_t)lam[k] : 0x3F80u;  // 1.0 past K
+    }
+  };
+  auto load_lam_w = [&](int u, u32x4_t (&dst)[US][2]) {
+#pragma unroll
+    for (int c = 0; c < US; ++c) {
+      const int k0 = u * UC + 64 * c + 16 * qd;
+      const int kk = k0 < K ? k0 : 0;
+      dst[c][0] = *reinterpret_cast<const u32x4_t*>(lam + kk);
+      dst[c][1] = *reinterpret_cast<const u32x4_t*>(lam + kk + 8);
+    }
+  };
+  // proj_down rows k0 .. k0 + 63 (all RP columns, zero past K or R): chunk i of the lane is
+  // row (lane + 64 i) / (RP / 8), columns 8 * ((lane + 64 i) % (RP / 8)) .. +8
+  auto load_pd = [&](int kstep, u32x4_t (&dst)[PDV]) {
+    if constexpr (LORA) {
+      const int k0 = kstep * 64;
+      const bool full = (R == RP) && (k0 + 64 <= K) && ((R & 7) == 0);
+#pragma unroll
+      for (int i = 0; i < PDV; ++i) {
+        const int ch = lane + 64 * i;
+        const int r_ = ch / (RP / 8), c8 = 8 * (ch % (RP / 8));
+        const int k = k0 + r_;
+        if (full) {
+          dst[i] = *reinterpret_cast<const u32x4_t*>(pd + (size_t)k * R + c8);
         } else {
-          v[s][2 * i] = x0 * l0;  // bf16 * bf16 is exact in float32
-          v[s][2 * i + 1] = x1 * l1;
-        }
-      }
-      if (ACT && RB > 0) {
-        // --- low-rank down-projection on the unrotated x_s -------------------------
-        const int k0 = u * COLS + 32 * s;
-        uint16_t* my_pd = pd_lds + wave * 32 * RP;
-        wave_lds_sync();
-        if (pd_vec) {  // 16-byte aligned rows of 8 consecutive ranks
-          for (int e = lane * 8; e < 32 * RP; e += 64 * 8) {
-            const int r_ = e / RP, c_ = e % RP;  // 8 consecutive columns of one row
-            u32x4_t val = {0u, 0u, 0u, 0u};
-            if (k0 + r_ < K && c_ < R) val = *reinterpret_cast<const u32x4_t*>(pd + (size_t)(k0 + r_) * R + c_);
-            *reinterpret_cast<u32x4_t*>(my_pd + e) = val;
+          uint32_t w[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int c0 = c8 + 2 * e2;
+            const uint32_t lo = (k < K && c0 < R) ? (uint32_t)pd[(size_t)k * R + c0] : 0u;
+            const uint32_t hi = (k < K && c0 + 1 < R) ? (uint32_t)pd[(size_t)k * R + c0 + 1] : 0u;
+            w[e2] = lo | (hi << 16);
           }
-        } else {
-          for (int e = lane; e < 32 * RP; e += 64) {
-            const int r_ = e / RP, c_ = e % RP;
-            uint16_t val = 0;
-            if (k0 + r_ < K && c_ < R) val = pd[(size_t)(k0 + r_) * R + c_];
-            my_pd[e] = val;
-          }
-        }
-        wave_lds_sync();
-        bf16x8_t hi, lo;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float f = v[s][i];
-          const uint32_t hb = f32_to_bf16_bits(f);
-          const float rem = f - bf16_bits_to_f32(hb);  // exact
-          hi[i] = bf16_from_bits(hb);
-          lo[i] = bf16_from_bits(f32_to_bf16_bits(rem));
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          bf16x8_t b;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) b[i] = bf16_from_bits(my_pd[(8 * oct + i) * RP + rb * 16 + row]);
-          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[rb], 0, 0, 0);
-          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[rb], 0, 0, 0);
+          dst[i] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
       }
     }
-    if (HB > 0) fwht_unit<HB, S>(v, oct);
+  };
+
+  u32x4_t xr[US][2];
+  u32x4_t lwr[ACT ? 1 : US][2];    // weights: lambda of the lane's columns
+  uint32_t lar[ACT ? US : 1];      // activations: lambda of column lane
+  u32x4_t pdr[PDV];
+  if (u_begin < u_end) {
+    load_x(u_begin, xr);
+    if constexpr (ACT) load_lam_act(u_begin, lar); else load_lam_w(u_begin, lwr);
+    load_pd(u_begin * US, pdr);
+  }
+
+  for (int u = u_begin; u < u_end; ++u) {
+    // current unit's raw inputs; prefetch the next unit's
+    u32x4_t xc[US][2];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int kk = u * COLS + 32 * s + 8 * oct;
-      const bool k_ok = kk < K;
-      const bool do_store = k_ok && row_ok;
-      uint8_t* sp = scales + (size_t)(kk >> 4) * M + (row_ok ? m : 0);
-      quantize_store(v[s], do_store, do_store && (oct & 1) == 0, qrow, (size_t)(kk >> 1), sp);
+    for (int c = 0; c < US; ++c) { xc[c][0] = xr[c][0]; xc[c][1] = xr[c][1]; }
+    uint32_t lac[ACT ? US : 1];
+    u32x4_t lwc[ACT ? 1 : US][2];
+    if constexpr (ACT) {
+#pragma unroll
+      for (int c = 0; c < US; ++c) lac[c] = lar[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < US; ++c) { lwc[c][0] = lwr[c][0]; lwc[c][1] = lwr[c][1]; }
+    }
+    if (u + 1 < u_end) {
+      load_x(u + 1, xr);
+      if constexpr (ACT) load_lam_act(u + 1, lar); else load_lam_w(u + 1, lwr);
+    }
+    const bool tail = (u + 1) * UC > K;
+    if (tail) {  // zero the columns past K (whole blocks, K being a multiple of the block)
+#pragma unroll
+      for (int c = 0; c < US; ++c)
+        if (u * UC + 64 * c + 16 * qd >= K) {
+          xc[c][0] = u32x4_t{0u, 0u, 0u, 0u};
+          xc[c][1] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+
+    float v[US][16];
+    if constexpr (ACT) {
+      // lambda and RN(1/lambda) of the unit's columns, shared through the wave's LDS
+      bool lam_ok = true;
+#pragma unroll
+      for (int c = 0; c < US; ++c) {
+        const float lf = bf16_bits_to_f32(lac[c]);
+        lam_ok &= (lf >= 0x1p-32f) && (lf <= 0x1p32f);
+        lam_s[64 * c + lane] = lf;
+        rlam_s[64 * c + lane] = __fdiv_rn(1.0f, lf);
+      }
+      u16x2_t mn = {0xFFFFu, 0xFFFFu}, mx = {0u, 0u};
+#pragma unroll
+      for (int c = 0; c < US; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) range_acc(xc[c][h][i], mn, mx);
+      const bool fast = __builtin_amdgcn_ballot_w64(!lam_ok || range_bad(mn, mx)) == 0;
+      wave_lds_sync();
+#pragma unroll
+      for (int c = 0; c < US; ++c) {
+        const float* ls = lam_s + 64 * c + 16 * qd;
+        const float* rl = rlam_s + 64 * c + 16 * qd;
+        float lv[16], rv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4_t a = *reinterpret_cast<const float4_t*>(ls + 4 * i);
+          const float4_t b = *reinterpret_cast<const float4_t*>(rl + 4 * i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { lv[4 * i + e] = a[e]; rv[4 * i + e] = b[e]; }
+        }
+        if (fast) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t d = xc[c][h][i];
+              const int j = 8 * h + 2 * i;
+              v[c][j] = div_markstein(__uint_as_float(d << 16), lv[j], rv[j]);
+              v[c][j + 1] = div_markstein(__uint_as_float(d & 0xFFFF0000u), lv[j + 1], rv[j + 1]);
+            }
+        } else {  // inputs outside the proven range somewhere in the wave: IEEE division
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t d = xc[c][h][i];
+              const int j = 8 * h + 2 * i;
+              v[c][j] = __fdiv_rn(__uint_as_float(d << 16), lv[j]);
+              v[c][j + 1] = __fdiv_rn(__uint_as_float(d & 0xFFFF0000u), lv[j + 1]);
+            }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < US; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t d = xc[c][h][i], l = lwc[c][h][i];
+            const int j = 8 * h + 2 * i;
+            v[c][j] = __uint_as_float(d << 16) * __uint_as_float(l << 16);  // bf16 * bf16: exact
+            v[c][j + 1] = __uint_as_float(d & 0xFFFF0000u) * __uint_as_float(l & 0xFFFF0000u);
+          }
+    }
+
+    if constexpr (LORA) {
+      // ---- low-rank down-projection on the unrotated x_s ------------------------------------
+#pragma unroll
+      for (int c = 0; c < US; ++c) {
+        const int kstep = u * US + c;
+        // stage this step's proj_down rows (the wave's previous reads are done: LDS is in order)
+#pragma unroll
+        for (int i = 0; i < PDV; ++i) {
+          const int ch = lane + 64 * i;
+          const int r_ = ch / (RP / 8), c8 = 8 * (ch % (RP / 8));
+          *reinterpret_cast<u32x4_t*>(pd_s + r_ * RS + c8) = pdr[i];
+        }
+        if (kstep + 1 < u_end * US) load_pd(kstep + 1, pdr);
+        wave_lds_sync();
+        bf16x8_t hi[2], lo[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float f0 = v[c][8 * h + 2 * j], f1 = v[c][8 * h + 2 * j + 1];
+            const bf16x2_t hb = __builtin_convertvector(float2_t{f0, f1}, bf16x2_t);
+            const uint32_t hbits = __builtin_bit_cast(uint32_t, hb);
+            const float r0 = f0 - __uint_as_float(hbits << 16);  // exact
+            const float r1 = f1 - __uint_as_float(hbits & 0xFFFF0000u);
+            const bf16x2_t lb = __builtin_convertvector(float2_t{r0, r1}, bf16x2_t);
+            hi[h][2 * j] = hb[0]; hi[h][2 * j + 1] = hb[1];
+            lo[h][2 * j] = lb[0]; lo[h][2 * j + 1] = lb[1];
+          }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            // lane (n = lane % 16, quarter qd) receives proj_down[16 qd + 8 h + 4 t + e][16 rb + n]
+            const int s = lane & 15;
+            const int base = (16 * qd + 8 * h + (s >> 2)) * RS + 16 * rb + 4 * (s & 3);
+            typedef __attribute__((address_space(3))) short4_t lds_s4;
+            const short4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(pd_s + base));
+            const short4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(pd_s + base + 4 * RS));
+            const u32x2_t w0 = __builtin_bit_cast(u32x2_t, t0), w1 = __builtin_bit_cast(u32x2_t, t1);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[h], b, acc[rb], 0, 0, 0);
+            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[h], b, acc[rb], 0, 0, 0);
+          }
+      }
+    }
+
+    if constexpr (HB > 0) fwht_unit<HB, US>(v);
+
+#pragma unroll
+    for (int c = 0; c < US; ++c) {
+      const int k0 = u * UC + 64 * c + 16 * qd;
+      u32x2_t codes;
+      uint32_t s8;
+      quantize_group(v[c], rtab, codes, s8);
+      if (row_ok && k0 < K) {
+        uint32_t* qp = reinterpret_cast<uint32_t*>(qrow + (k0 >> 1));  // 4-byte aligned output
+        qp[0] = codes[0];
+        qp[1] = codes[1];
+        scales[(size_t)(k0 >> 4) * M + m] = (uint8_t)s8;
+      }
     }
   }
 
-  if (ACT && RB > 0) {
-    // --- deterministic cross-wave reduction of the low-rank partials -------------------
-    float* my_red = red_lds + wave * QROWS * RP;
+  if constexpr (LORA) {
+    // ---- deterministic cross-wave reduction of the low-rank partials ----------------------
+    __syncthreads();  // every wave is done with its proj_down staging area
+    float* red = reinterpret_cast<float*>(smem + 512);
+    float* my_red = red + wave * QROWS * RP;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) my_red[(oct * 4 + j) * RP + rb * 16 + row] = acc[rb][j];
+      for (int e = 0; e < 4; ++e) my_red[(4 * qd + e) * RP + 16 * rb + row] = acc[rb][e];
     __syncthreads();
     for (int t = threadIdx.x; t < QROWS * R; t += blockDim.x) {
       const int rr = t / R, cc = t % R;
       float sum = 0.0f;
-      for (int w = 0; w < nwaves; ++w) sum += red_lds[w * QROWS * RP + rr * RP + cc];
-      const int mm = blockIdx.x * QROWS + rr;
+      for (int w = 0; w < nwaves; ++w) sum += red[w * QROWS * RP + rr * RP + cc];
+      const int mm = m0 + rr;
       if (mm < M) lora[(size_t)blockIdx.y * M * R + (size_t)mm * R + cc] = sum;
     }
   }
 }
 
-template <int HB, bool ACT>
-hipError_t launch_rb(int rb, dim3 grid, dim3 block, hipStream_t st, const uint16_t* x, const uint16_t* lam,
-                     const uint16_t* pd, int M, int K, int R, int pd_vec, int upw, int nunits, uint8_t* q,
-                     uint8_t* sc, float* lora) {
-  switch (rb) {
-    case 0: quantize_kernel<HB, ACT, 0><<<grid, block, 0, st>>>(x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora); break;
-    case 1: quantize_kernel<HB, ACT, 1><<<grid, block, 0, st>>>(x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora); break;
-    case 2: quantize_kernel<HB, ACT, 2><<<grid, block, 0, st>>>(x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora); break;
-    case 3: quantize_kernel<HB, ACT, 3><<<grid, block, 0, st>>>(x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora); break;
-    default: quantize_kernel<HB, ACT, 4><<<grid, block, 0, st>>>(x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora); break;
-  }
+template <int HB, bool ACT, int RB>
+hipError_t launch_one(dim3 grid, int nunits, int per_part, hipStream_t st, const uint16_t* x, const uint16_t* lam,
+                      const uint16_t* pd, int M, int K, int R, uint8_t* q, uint8_t* sc, float* lora) {
+  using C = QCfg<HB, ACT, RB>;
+  int nwaves = per_part < C::WAVES ? per_part : C::WAVES;
+  if (nwaves < 1) nwaves = 1;
+  const int upw = (per_part + nwaves - 1) / nwaves;
+  nwaves = (per_part + upw - 1) / upw;
+  if (nwaves < 1) nwaves = 1;
+  quantize_kernel<HB, ACT, RB><<<grid, dim3(64 * nwaves), 0, st>>>(x, lam, pd, M, K, R, upw, nunits, q, sc, lora);
   return hipGetLastError();
 }
 
+template <int HB, bool ACT>
+hipError_t launch_rb(int rb, dim3 grid, int nunits, int per_part, hipStream_t st, const uint16_t* x,
+                     const uint16_t* lam, const uint16_t* pd, int M, int K, int R, uint8_t* q, uint8_t* sc,
+                     float* lora) {
+  switch (rb) {
+    case 0: return launch_one<HB, ACT, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+    case 1: return launch_one<HB, ACT, 1>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+    case 2: return launch_one<HB, ACT, 2>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+    case 3: return launch_one<HB, ACT, 3>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+    default: return launch_one<HB, ACT, 4>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+  }
+}
+
 template <bool ACT>
-hipError_t launch_hb(int hb, int rb, dim3 grid, dim3 block, hipStream_t st, const uint16_t* x,
-                     const uint16_t* lam, const uint16_t* pd, int M, int K, int R, int pd_vec, int upw,
-                     int nunits, uint8_t* q, uint8_t* sc, float* lora) {
-  switch (hb) {
-    case 0: return launch_rb<0, ACT>(rb, grid, block, st, x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora);
-    case 16: return launch_rb<16, ACT>(rb, grid, block, st, x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora);
-    case 32: return launch_rb<32, ACT>(rb, grid, block, st, x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora);
-    case 64: return launch_rb<64, ACT>(rb, grid, block, st, x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora);
-    default: return launch_rb<128, ACT>(rb, grid, block, st, x, lam, pd, M, K, R, pd_vec, upw, nunits, q, sc, lora);
+hipError_t launch_hb(int hb, int rb, dim3 grid, int nunits, int per_part, hipStream_t st, const uint16_t* x,
+                     const uint16_t* lam, const uint16_t* pd, int M, int K, int R, uint8_t* q, uint8_t* sc,
+                     float* lora) {
+  if constexpr (ACT) {
+    switch (hb) {
+      case 0: return launch_rb<0, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      case 16: return launch_rb<16, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      case 32: return launch_rb<32, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      case 64: return launch_rb<64, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      default: return launch_rb<128, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+    }
+  } else {
+    switch (hb) {
+      case 0: return launch_one<0, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      case 16: return launch_one<16, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      case 32: return launch_one<32, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      case 64: return launch_one<64, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      default: return launch_one<128, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+    }
   }
 }
 
@@ -286,32 +551,25 @@ hipError_t launch_hb(int hb, int rb, dim3 grid, dim3 block, hipStream_t st, cons
 int quantize_parts(int64_t M, int64_t K) {
   // Small batches split K across workgroups so that enough CUs stream x; the partial
   // low-rank sums are added in a fixed order by the consumer.
-  const int64_t n32 = K / 32;
-  if (M > SKINNY_MAX_M || n32 < 32) return 1;
-  return (int)(n32 / 16 < 8 ? n32 / 16 : 8);
+  const int64_t n64 = K / 64;
+  if (M > SKINNY_MAX_M || n64 < 16) return 1;
+  return (int)(n64 / 8 < 8 ? n64 / 8 : 8);
 }
 
 hipError_t launch_quantize(bool act, const void* x, const void* lam, const void* pd, int64_t M, int64_t K,
                            int64_t R, int hb, int parts, void* q, void* scales, float* lora, hipStream_t stream) {
-  const int cols = hb > 32 ? hb : 32;
-  const int nunits = (int)((K + cols - 1) / cols);
+  const int uc = hb == 128 ? 128 : 64;
+  const int nunits = (int)((K + uc - 1) / uc);
   const int per_part = (nunits + parts - 1) / parts;
-  int nwaves = per_part < QMAX_WAVES ? per_part : QMAX_WAVES;
-  const int upw = (per_part + nwaves - 1) / nwaves;
-  nwaves = (per_part + upw - 1) / upw;
   const int rb = act ? (int)((R + 15) / 16) : 0;
   dim3 grid((unsigned)((M + QROWS - 1) / QROWS), (unsigned)parts);
-  dim3 block((unsigned)(64 * nwaves));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* lp = static_cast<const uint16_t*>(lam);
   const uint16_t* pp = static_cast<const uint16_t*>(pd);
   uint8_t* qp = static_cast<uint8_t*>(q);
   uint8_t* sp = static_cast<uint8_t*>(scales);
-  const int pd_vec = (R % 8 == 0) && ((reinterpret_cast<uintptr_t>(pd) & 15) == 0);
-  if (act)
-    return launch_hb<true>(hb, rb, grid, block, stream, xp, lp, pp, (int)M, (int)K, (int)R, pd_vec, upw, nunits, qp,
-                           sp, lora);
-  return launch_hb<false>(hb, 0, grid, block, stream, xp, lp, pp, (int)M, (int)K, 0, 0, upw, nunits, qp, sp, nullptr);
+  if (act) return launch_hb<true>(hb, rb, grid, nunits, per_part, stream, xp, lp, pp, (int)M, (int)K, (int)R, qp, sp, lora);
+  return launch_hb<false>(hb, 0, grid, nunits, per_part, stream, xp, lp, pp, (int)M, (int)K, 0, qp, sp, nullptr);
 }
 
 }  // namespace w4a4

@@ -28,8 +28,10 @@
 //
 // Epilogue: acc *= wcscales[n] * wtscale; the rank-R correction is
 // accumulated on the matrix cores (bf16 32x32x16, L split into bf16 hi + lo
-// parts, proj_up exact in bf16); the tile is rounded to bf16 (nearest even),
-// transposed through LDS and written with 16-byte row-contiguous stores.
+// parts, proj_up exact in bf16); each lane rounds its values to bf16 (nearest
+// even) and stores 4 consecutive n of one m as one 8-byte write.  The epilogue
+// operands of the tile (L summed over its partial sums and split into bf16 hi +
+// lo, proj_up, wcscales * wtscale) are first staged in LDS with coalesced loads.
 #include <cstdlib>
 #include <cstring>
 
@@ -55,7 +57,10 @@ struct Tile {
   static constexpr int SB_PT = (2 * BN + THREADS - 1) / THREADS;
   static constexpr int SCALE_BYTES = 8 * ROWS * 2;  // f16 scales laid out [group][row]
   static constexpr int STAGE_BYTES = ROWS * CODE_STRIDE + SCALE_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  // epilogue operands staged after the K loop: L hi and lo parts [BM][64] bf16, proj_up
+  // [BN][64] bf16, column scale [BN] f32 (rank padded to the compiled maximum 64)
+  static constexpr int EPI_BYTES = BM * 64 * 2 * 2 + BN * 64 * 2 + BN * 4;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_BYTES ? 2 * STAGE_BYTES : EPI_BYTES;
 };
 
 // Global -> register -> LDS staging of one K-step.  Per-thread offsets are loop invariant;
@@ -321,51 +326,85 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   }
 
   // ---- epilogue -------------------------------------------------------------------------
+  // The K loop ended with a barrier, so the stage buffers are free: stage the tile's epilogue
+  // operands there with coalesced loads, then read them per lane from LDS.
   // acc[i][j][4q + e] is y[m, n] with m = mb + i*32 + l32, n = nb + j*32 + 8q + 4h + e.
   const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
-  const float ts = bf16_bits_to_f32(wts[0]);
+  constexpr int RS = 64;  // rank stride of the staged operands (compiled maximum rank)
+  uint16_t* l_hi = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* l_lo = l_hi + T::BM * RS;
+  uint16_t* p_lds = l_lo + T::BM * RS;
+  float* c_lds = reinterpret_cast<float*>(p_lds + T::BN * RS);
+  const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank actually used
+  {
+    const float ts = bf16_bits_to_f32(wts[0]);
+    for (int c = t; c < T::BN; c += T::THREADS) {
+      const int n = n0 + c;
+      c_lds[c] = n < N ? bf16_bits_to_f32(wcs[n]) * ts : 0.0f;
+    }
+    if (LORA) {
+      // one block of 16 ranks at a time; each thread issues all its loads of the block first
+      constexpr int LI = (T::BM * 16 + T::THREADS - 1) / T::THREADS;
+      constexpr int PI = (T::BN * 16 + T::THREADS - 1) / T::THREADS;
+      for (int r0 = 0; r0 < rp; r0 += 16) {
+        float f[LI];
+        uint32_t pw[PI];
+#pragma unroll
+        for (int u = 0; u < LI; ++u) {
+          const int idx = t + u * T::THREADS;
+          const int rr = min(idx >> 4, T::BM - 1), r = r0 + (idx & 15);
+          const size_t at = (size_t)min(m0 + rr, M - 1) * R + (r < R ? r : 0);
+          float acc_l = 0.0f;
+          for (int p = 0; p < parts; ++p) acc_l += lora[(size_t)p * M * R + at];
+          f[u] = r < R ? acc_l : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < PI; ++u) {
+          const int idx = t + u * T::THREADS;
+          const int rr = min(idx >> 4, T::BN - 1), r = r0 + (idx & 15);
+          const uint32_t v = pu[(size_t)min(n0 + rr, N - 1) * R + (r < R ? r : 0)];
+          pw[u] = r < R ? v : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < LI; ++u) {
+          const int idx = t + u * T::THREADS;
+          if ((T::BM * 16) % T::THREADS == 0 || idx < T::BM * 16) {
+            const int rr = idx >> 4, r = r0 + (idx & 15);
+            const uint32_t hb = f32_to_bf16_bits(f[u]);
+            l_hi[rr * RS + r] = (uint16_t)hb;
+            l_lo[rr * RS + r] = (uint16_t)f32_to_bf16_bits(f[u] - bf16_bits_to_f32(hb));  // exact remainder
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < PI; ++u) {
+          const int idx = t + u * T::THREADS;
+          if ((T::BN * 16) % T::THREADS == 0 || idx < T::BN * 16) p_lds[(idx >> 4) * RS + r0 + (idx & 15)] = (uint16_t)pw[u];
+        }
+      }
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < FN; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n = nb + j * 32 + 8 * q + 4 * h + e;
-        const float c = n < N ? bf16_bits_to_f32(wcs[n < N ? n : 0]) * ts : 0.0f;
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c;
-      }
+        for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
     }
   if (LORA) {
-    const int nrb = (R + 15) / 16;
-    for (int rb = 0; rb < nrb; ++rb) {
+    for (int r0 = 0; r0 < rp; r0 += 16) {
       bf16x8_t pv[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = nb + j * 32 + l32;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = rb * 16 + 8 * h + e;
-          const bool ok = n < N && r < R;
-          const uint32_t b = pu[ok ? (size_t)n * R + r : 0];
-          pv[j][e] = bf16_from_bits(ok ? b : 0u);
-        }
-      }
+      for (int j = 0; j < FN; ++j)
+        pv[j] = *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * RS + r0 + 8 * h);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int m = mb + i * 32 + l32;
-        bf16x8_t lhi, llo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = rb * 16 + 8 * h + e;
-          const bool ok = m < M && r < R;
-          float f0 = 0.0f;
-          for (int p = 0; p < parts; ++p) f0 += lora[ok ? (size_t)p * M * R + (size_t)m * R + r : 0];
-          const float f = ok ? f0 : 0.0f;
-          const uint32_t hb = f32_to_bf16_bits(f);
-          lhi[e] = bf16_from_bits(hb);
-          llo[e] = bf16_from_bits(f32_to_bf16_bits(f - bf16_bits_to_f32(hb)));
-        }
+        const int row = wm * FM * 32 + i * 32 + l32;
+        const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * RS + r0 + 8 * h);
+        const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * RS + r0 + 8 * h);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);

@@ -44,12 +44,15 @@ typedef enum {
   W4A4_ERR_SHAPE = 2,       /* a size is negative, K % 16 != 0, K % block != 0,
                                or the workspace is too small                      */
   W4A4_ERR_ALIGN = 3,       /* a pointer breaks its required alignment            */
-  W4A4_ERR_UNSUPPORTED = 4, /* hadamard_block not in {0,16,32,64,128} or R > 64   */
+  W4A4_ERR_UNSUPPORTED = 4, /* hadamard_block not in {0,16,32,64,128}, R > 64, or K > W4A4_MAX_K */
   W4A4_ERR_HIP = 5          /* the HIP runtime reported an error at launch        */
 } w4a4_status;
 
 /* Largest supported correction rank R. */
 #define W4A4_MAX_RANK 64
+/* Largest supported K (2^24 columns): the kernels address a tile's rows x K/2 code bytes with
+   32-bit offsets. */
+#define W4A4_MAX_K (1 << 24)
 
 /* Human-readable name of a status code (static storage). */
 const char* w4a4_status_string(int status);

@@ -59,6 +59,7 @@ def test_quantize_act_validation(lib):
     assert _qa(lib, M=-1) == ERR_SHAPE
     assert _qa(lib, R=-1) == ERR_SHAPE
     assert _qa(lib, R=65) == ERR_UNSUPPORTED
+    assert _qa(lib, K=(1 << 24) + 16) == ERR_UNSUPPORTED
     assert _qa(lib, hb=8) == ERR_UNSUPPORTED
     assert _qa(lib, hb=256) == ERR_UNSUPPORTED
     assert _qa(lib, K=48, hb=32) == ERR_SHAPE
@@ -88,6 +89,7 @@ def test_gemm_validation(lib):
     assert _gemm(lib, K=8) == ERR_SHAPE
     assert _gemm(lib, N=-3) == ERR_SHAPE
     assert _gemm(lib, R=100) == ERR_UNSUPPORTED
+    assert _gemm(lib, K=(1 << 24) + 16) == ERR_UNSUPPORTED
     assert _gemm(lib, qa=P + 4) == ERR_ALIGN
     assert _gemm(lib, qw=P + 8) == ERR_ALIGN
     assert _gemm(lib, y=P + 1) == ERR_ALIGN

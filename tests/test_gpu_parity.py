@@ -143,10 +143,13 @@ def test_gemm_lowrank_parity(w4, M, N, K, R):
 GEMM_VARIANTS = ["2x2x4x4", "2x2x4x3", "2x2x4x2", "2x2x2x2", "4x2x2x4", "2x4x4x2", "4x2x2x3"]
 
 
+@pytest.mark.parametrize("path", ["dma", "stage"])
 @pytest.mark.parametrize("variant", GEMM_VARIANTS)
-def test_gemm_every_tile_variant(w4, variant, monkeypatch):
-    """Each compiled tile layout, forced through W4A4_GEMM_TILE, on a shape with ragged edges."""
+def test_gemm_every_tile_variant(w4, variant, path, monkeypatch):
+    """Each compiled tile layout of both K pipelines (direct LDS loads, and register staging forced
+    through W4A4_GEMM_PATH), forced through W4A4_GEMM_TILE, on a shape with ragged edges."""
     monkeypatch.setenv("W4A4_GEMM_TILE", variant)
+    monkeypatch.setenv("W4A4_GEMM_PATH", path)
     lay = synth.make_layer("tiny", seed=31, M=300, K=640, N=520, R=32, B=0, wcs="uniform")
     _check_gemm(w4, lay)
 

@@ -9,6 +9,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;  // sizes are indexed with 32-bit ints in the kernels
+constexpr int64_t kMaxK = W4A4_MAX_K;     // tile-local byte offsets (rows x K/2) are 32-bit
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -16,7 +17,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 w4a4_status check_k_rank_block(int64_t K, int64_t R, int32_t hb) {
   if (hb != 0 && hb != 16 && hb != 32 && hb != 64 && hb != 128) return W4A4_ERR_UNSUPPORTED;
-  if (R > W4A4_MAX_RANK) return W4A4_ERR_UNSUPPORTED;
+  if (R > W4A4_MAX_RANK || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
   if (K < 16 || K % 16 != 0 || K > kMaxDim || R < 0) return W4A4_ERR_SHAPE;
   if (hb != 0 && K % hb != 0) return W4A4_ERR_SHAPE;
   return W4A4_OK;
@@ -65,7 +66,7 @@ const char* w4a4_status_string(int status) {
     case W4A4_ERR_NULL: return "a required pointer is NULL";
     case W4A4_ERR_SHAPE: return "invalid sizes (negative, K % 16 != 0, K % hadamard_block != 0, or workspace too small)";
     case W4A4_ERR_ALIGN: return "a pointer breaks its required alignment";
-    case W4A4_ERR_UNSUPPORTED: return "unsupported hadamard_block or rank above the compiled maximum";
+    case W4A4_ERR_UNSUPPORTED: return "unsupported hadamard_block, or rank or K above the compiled maximum";
     case W4A4_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }

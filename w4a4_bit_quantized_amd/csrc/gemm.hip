@@ -48,6 +48,7 @@ constexpr int CODE_STRIDE = 80;    // LDS bytes per code row: 64 data + 16 pad (
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 struct Tile {
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int WM = WAVES_M, WN = WAVES_N, FRAG_M = FM, FRAG_N = FN;
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;
   static constexpr int ROWS = BM + BN;  // activation rows, then weight rows, in LDS
@@ -57,11 +58,69 @@ struct Tile {
   static constexpr int SB_PT = (2 * BN + THREADS - 1) / THREADS;
   static constexpr int SCALE_BYTES = 8 * ROWS * 2;  // f16 scales laid out [group][row]
   static constexpr int STAGE_BYTES = ROWS * CODE_STRIDE + SCALE_BYTES;
-  // epilogue operands staged after the K loop: L hi and lo parts [BM][64] bf16, proj_up
-  // [BN][64] bf16, column scale [BN] f32 (rank padded to the compiled maximum 64)
+  // Epilogue operands, staged in the stage buffers after the K loop: L hi and lo parts
+  // [BM][64] bf16, proj_up [BN][64] bf16 and the column scale [BN] f32.
   static constexpr int EPI_BYTES = BM * 64 * 2 * 2 + BN * 64 * 2 + BN * 4;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_BYTES ? 2 * STAGE_BYTES : EPI_BYTES;
 };
+
+// Stage a tile's epilogue operands in LDS: the column scales wcscales * wtscale, and for the
+// ranks [0, rp) the low-rank activations summed over their `parts` partial sums (in order) and
+// split into bf16 hi + lo parts, and proj_up.  Padded ranks and rows past M or N are zero or
+// clamped.  Each thread issues all its loads of a 16-rank block before storing any of them.
+template <class T, bool LORA>
+__device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int rp, int t, int m0, int n0, int M, int N,
+                                               int R, int parts, const float* __restrict__ lora,
+                                               const uint16_t* __restrict__ pu, const uint16_t* __restrict__ wcs,
+                                               const uint16_t* __restrict__ wts) {
+  uint16_t* l_hi = reinterpret_cast<uint16_t*>(base);
+  uint16_t* l_lo = l_hi + T::BM * rs;
+  uint16_t* p_lds = l_lo + T::BM * rs;
+  float* c_lds = reinterpret_cast<float*>(p_lds + T::BN * rs);
+  const float ts = bf16_bits_to_f32(wts[0]);
+  for (int c = t; c < T::BN; c += T::THREADS) {
+    const int n = n0 + c;
+    c_lds[c] = n < N ? bf16_bits_to_f32(wcs[n]) * ts : 0.0f;
+  }
+  if (!LORA) return;
+  constexpr int LI = (T::BM * 16 + T::THREADS - 1) / T::THREADS;
+  constexpr int PI = (T::BN * 16 + T::THREADS - 1) / T::THREADS;
+  for (int r0 = 0; r0 < rp; r0 += 16) {
+    float f[LI];
+    uint32_t pw[PI];
+#pragma unroll
+    for (int u = 0; u < LI; ++u) {
+      const int idx = t + u * T::THREADS;
+      const int rr = min(idx >> 4, T::BM - 1), r = r0 + (idx & 15);
+      const size_t at = (size_t)min(m0 + rr, M - 1) * R + (r < R ? r : 0);
+      float acc_l = 0.0f;
+      for (int p = 0; p < parts; ++p) acc_l += lora[(size_t)p * M * R + at];
+      f[u] = r < R ? acc_l : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < PI; ++u) {
+      const int idx = t + u * T::THREADS;
+      const int rr = min(idx >> 4, T::BN - 1), r = r0 + (idx & 15);
+      const uint32_t v = pu[(size_t)min(n0 + rr, N - 1) * R + (r < R ? r : 0)];
+      pw[u] = r < R ? v : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < LI; ++u) {
+      const int idx = t + u * T::THREADS;
+      if ((T::BM * 16) % T::THREADS == 0 || idx < T::BM * 16) {
+        const int rr = idx >> 4, r = r0 + (idx & 15);
+        const uint32_t hb = f32_to_bf16_bits(f[u]);
+        l_hi[rr * rs + r] = (uint16_t)hb;
+        l_lo[rr * rs + r] = (uint16_t)f32_to_bf16_bits(f[u] - bf16_bits_to_f32(hb));  // exact remainder
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PI; ++u) {
+      const int idx = t + u * T::THREADS;
+      if ((T::BN * 16) % T::THREADS == 0 || idx < T::BN * 16) p_lds[(idx >> 4) * rs + r0 + (idx & 15)] = (uint16_t)pw[u];
+    }
+  }
+}
 
 // Global -> register -> LDS staging of one K-step.  Per-thread offsets are loop invariant;
 // each K-step only moves the uniform base pointers.  Rows past M (or N) read a clamped valid
@@ -217,6 +276,117 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// One K-step of a wave from its operands already in registers: 8 sub-steps, each one
+// v_mfma_f32_32x32x16_f16 per (i, j) fragment pair; sub-step kk + 1 is decoded while the MFMAs
+// of sub-step kk run.  Sub-step kk covers K-columns 64h + 8kk .. +8 of the stage (lane half h),
+// the codes of dword kk & 3 of 16-byte half kk >> 2 and the scale of group 4h + kk / 2.
+template <int FM, int FN>
+__device__ __forceinline__ void mma_stage(float16_t (&acc)[FM][FN], const uint32_t (&sA)[FM][2],
+                                          const uint32_t (&sB)[FN][2], const u32x4_t (&cA)[2][FM],
+                                          const u32x4_t (&cB)[2][FN]) {
+  half8_t av[FM], bv[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) av[i] = decode8(cA[0][i][0], scale_pair(sA[i][0], 0));
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bv[j] = decode8(cB[0][j][0], scale_pair(sB[j][0], 0));
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    half8_t an[FM], bn[FN];
+    if (kk < 7) {
+      const int k1 = kk + 1, hf = k1 >> 2, q = k1 & 3, g = k1 >> 1;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) an[i] = decode8(cA[hf][i][q], scale_pair(sA[i][g >> 1], g & 1));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bn[j] = decode8(cB[hf][j][q], scale_pair(sB[j][g >> 1], g & 1));
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[i][j], 0, 0, 0);
+    if (kk < 7) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) av[i] = an[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bv[j] = bn[j];
+    }
+  }
+}
+
+// Epilogue of a tile: stage the operands in LDS (`lds` must be free; it is left in use), then
+// acc *= wcscales[n] * wtscale, add L @ proj_up^T on the matrix cores, round to bf16 and store.
+// acc[i][j][4q + e] is y[m, n] with m = mb + i*32 + l32, n = nb + j*32 + 8q + 4h + e.
+template <class T, bool LORA>
+__device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N], uint8_t* lds, int t, int m0,
+                                         int n0, int M, int N, int R, int parts, const float* __restrict__ lora,
+                                         const uint16_t* __restrict__ pu, const uint16_t* __restrict__ wcs,
+                                         const uint16_t* __restrict__ wts, uint16_t* __restrict__ y) {
+  constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
+  constexpr int rs = 64;  // rank stride of the staged operands (compiled maximum rank)
+  const int lane = t & 63, wave = t >> 6;
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank
+  stage_epilogue<T, LORA>(lds, rs, rp, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts);
+  __syncthreads();
+  const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
+  const uint16_t* l_hi = reinterpret_cast<const uint16_t*>(lds);
+  const uint16_t* l_lo = l_hi + T::BM * rs;
+  const uint16_t* p_lds = l_lo + T::BM * rs;
+  const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
+    }
+  if (LORA) {
+    for (int r0 = 0; r0 < rp; r0 += 16) {
+      bf16x8_t pv[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        pv[j] = *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * rs + r0 + 8 * h);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * FM * 32 + i * 32 + l32;
+        const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * rs + r0 + 8 * h);
+        const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], llo, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+  const bool n4 = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = mb + i * 32 + l32;
+    if (m >= M) continue;
+    uint16_t* yrow = y + (size_t)m * N;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb + j * 32 + 8 * q + 4 * h;
+        const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        if (n4) {
+          if (n < N) *reinterpret_cast<u32x2_t*>(yrow + n) = u32x2_t{p0, p1};
+        } else {
+          const uint16_t v[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) yrow[n + e] = v[e];
+        }
+      }
+  }
+}
+
 // The MFMA's first operand carries weight rows (output columns n) and its second operand
 // activation rows (output rows m): each lane's accumulator then holds 4 consecutive n of
 // one m per register quad, which is stored directly as 8 contiguous bytes of y.
@@ -242,14 +412,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   const int nkt = (K + BK - 1) / BK;
   const int nfull = kbytes / (BK / 2);  // K-steps with no column past K
 
-  float16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
   Stager<T, VEC16> st;
   const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);
   st.init(rows_a, rows_b, M, N, kbytes, t);
@@ -257,6 +419,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   else st.template load<true, SC4>(qa, qw, sa, sw, M, N, m0, n0, rows_a, rows_b, 0, kbytes, groups, t);
   st.store(lds, t);
   __syncthreads();
+
+  float16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   for (int kt = 0; kt < nkt; ++kt) {
     const bool more = kt + 1 < nkt;
@@ -293,149 +463,176 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
       cB[0][j] = *reinterpret_cast<const u32x4_t*>(codes_lds + row * CODE_STRIDE + 32 * h);
       cB[1][j] = *reinterpret_cast<const u32x4_t*>(codes_lds + row * CODE_STRIDE + 32 * h + 16);
     }
-    // Software pipeline over the 8 sub-steps: sub-step kk + 1 is decoded while the MFMAs of
-    // sub-step kk run.
-    half8_t av[FM], bv[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) av[i] = decode8(cA[0][i][0], scale_pair(sA[i][0], 0));
-#pragma unroll
-    for (int j = 0; j < FN; ++j) bv[j] = decode8(cB[0][j][0], scale_pair(sB[j][0], 0));
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      half8_t an[FM], bn[FN];
-      if (kk < 7) {
-        const int k1 = kk + 1, hf = k1 >> 2, q = k1 & 3, g = k1 >> 1;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) an[i] = decode8(cA[hf][i][q], scale_pair(sA[i][g >> 1], g & 1));
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bn[j] = decode8(cB[hf][j][q], scale_pair(sB[j][g >> 1], g & 1));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[i][j], 0, 0, 0);
-      if (kk < 7) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) av[i] = an[i];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bv[j] = bn[j];
-      }
-    }
+    mma_stage<FM, FN>(acc, sA, sB, cA, cB);
     if (more) st.store(lds + ((kt + 1) & 1) * T::STAGE_BYTES, t);
     __syncthreads();
   }
 
-  // ---- epilogue -------------------------------------------------------------------------
-  // The K loop ended with a barrier, so the stage buffers are free: stage the tile's epilogue
-  // operands there with coalesced loads, then read them per lane from LDS.
-  // acc[i][j][4q + e] is y[m, n] with m = mb + i*32 + l32, n = nb + j*32 + 8q + 4h + e.
-  const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
-  constexpr int RS = 64;  // rank stride of the staged operands (compiled maximum rank)
-  uint16_t* l_hi = reinterpret_cast<uint16_t*>(lds);
-  uint16_t* l_lo = l_hi + T::BM * RS;
-  uint16_t* p_lds = l_lo + T::BM * RS;
-  float* c_lds = reinterpret_cast<float*>(p_lds + T::BN * RS);
-  const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank actually used
-  {
-    const float ts = bf16_bits_to_f32(wts[0]);
-    for (int c = t; c < T::BN; c += T::THREADS) {
-      const int n = n0 + c;
-      c_lds[c] = n < N ? bf16_bits_to_f32(wcs[n]) * ts : 0.0f;
-    }
-    if (LORA) {
-      // one block of 16 ranks at a time; each thread issues all its loads of the block first
-      constexpr int LI = (T::BM * 16 + T::THREADS - 1) / T::THREADS;
-      constexpr int PI = (T::BN * 16 + T::THREADS - 1) / T::THREADS;
-      for (int r0 = 0; r0 < rp; r0 += 16) {
-        float f[LI];
-        uint32_t pw[PI];
+  // the K loop ended with a barrier: the stage buffers are free for the epilogue operands
+  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
+}
+
+// ---- three-stage variant with direct global -> LDS loads -----------------------------
+// For K a multiple of 128 and M, N multiples of 4.  Everything K-step kt + 2 needs is fetched
+// straight into LDS (global_load_lds: no VGPRs hold data in flight) while K-step kt is
+// computed, so two K-steps of latency are covered and the only waits are the explicit ones
+// ahead of each barrier.
+//  * Codes: each wave instruction (dwordx4) fills 1 KB = 16 rows of 64 bytes.  Chunk c of row r
+//    is placed at 16-byte position c ^ ((r >> 1) & 3), which keeps the operand reads of 8
+//    consecutive rows on distinct banks.
+//  * Scales: each lane moves one dword of the (K/16, rows) scale tensor (4 consecutive rows of
+//    one group); the dwords are laid out [row quad][8 groups], so a lane reads the 4 groups of
+//    its half with one 16-byte read and picks its row's byte out of each dword.
+// Rows past the tile's valid ones (and the padding up to whole instructions) read clamped
+// valid rows and are never stored.
+template <class T>
+struct DmaTile {
+  static constexpr int WAVES = T::WM * T::WN;
+  static constexpr int ROUND_ROWS = 16 * WAVES;  // code rows one instruction per wave covers
+  static constexpr int ROUNDS = (T::ROWS + ROUND_ROWS - 1) / ROUND_ROWS;
+  static constexpr int SDW = 2 * T::ROWS;        // scale dwords per K-step: ROWS/4 quads x 8 groups
+  static constexpr int SROUNDS = (SDW + 64 * WAVES - 1) / (64 * WAVES);
+  static constexpr int SCALE_OFF = ROUNDS * ROUND_ROWS * 64;
+  static constexpr int STAGE = SCALE_OFF + SROUNDS * WAVES * 256;
+  static constexpr int LOADS = ROUNDS + SROUNDS;  // load instructions per wave per K-step
+  static constexpr int LDS_BYTES = 3 * STAGE > T::EPI_BYTES ? 3 * STAGE : T::EPI_BYTES;
+  static_assert(T::BM % 16 == 0 && T::ROWS % 16 == 0, "whole 16-row blocks");
+};
+
+// Wait until at most N vector-memory operations of this wave are outstanding and all its LDS
+// operations are done, then join the workgroup barrier.  The compiler may not move memory
+// operations across it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue one K-step's direct loads of a wave: ROUNDS code instructions (16 bytes per lane) and
+// SROUNDS scale instructions (4 bytes per lane) into the stage at `stage`.
+template <class D>
+__device__ __forceinline__ void dma_issue(uint8_t* stage, int wave, uint32_t kb0, size_t g0,
+                                          const uint8_t* const* c_base, const uint32_t* c_off,
+                                          const uint8_t* const* s_base, const uint32_t* s_off,
+                                          const uint32_t* s_stride) {
 #pragma unroll
-        for (int u = 0; u < LI; ++u) {
-          const int idx = t + u * T::THREADS;
-          const int rr = min(idx >> 4, T::BM - 1), r = r0 + (idx & 15);
-          const size_t at = (size_t)min(m0 + rr, M - 1) * R + (r < R ? r : 0);
-          float acc_l = 0.0f;
-          for (int p = 0; p < parts; ++p) acc_l += lora[(size_t)p * M * R + at];
-          f[u] = r < R ? acc_l : 0.0f;
-        }
+  for (int r = 0; r < D::ROUNDS; ++r)
+    __builtin_amdgcn_global_load_lds(c_base[r] + kb0 + c_off[r],
+                                     (lds_void*)(stage + (r * D::ROUND_ROWS + wave * 16) * 64), 16, 0, 0);
 #pragma unroll
-        for (int u = 0; u < PI; ++u) {
-          const int idx = t + u * T::THREADS;
-          const int rr = min(idx >> 4, T::BN - 1), r = r0 + (idx & 15);
-          const uint32_t v = pu[(size_t)min(n0 + rr, N - 1) * R + (r < R ? r : 0)];
-          pw[u] = r < R ? v : 0u;
-        }
+  for (int r = 0; r < D::SROUNDS; ++r)
+    __builtin_amdgcn_global_load_lds(s_base[r] + g0 * s_stride[r] + s_off[r],
+                                     (lds_void*)(stage + D::SCALE_OFF + (r * D::WAVES + wave) * 256), 4, 0, 0);
+}
+
+template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
+    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
+    uint16_t* __restrict__ y) {
+  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
+  using D = DmaTile<T>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[D::LDS_BYTES];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int tiles_n = (N + T::BN - 1) / T::BN;
+  const int n0 = (int)(blockIdx.x % tiles_n) * T::BN;
+  const int m0 = (int)(blockIdx.x / tiles_n) * T::BM;
+  const uint32_t kbytes = (uint32_t)K / 2;
+  const int nkt = K / BK;
+  const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);  // multiples of 4
+
+  // code chunk of each round: tile row (clamped to a valid row) and swizzled 16-byte chunk
+  const uint8_t* c_base[D::ROUNDS];
+  uint32_t c_off[D::ROUNDS];
 #pragma unroll
-        for (int u = 0; u < LI; ++u) {
-          const int idx = t + u * T::THREADS;
-          if ((T::BM * 16) % T::THREADS == 0 || idx < T::BM * 16) {
-            const int rr = idx >> 4, r = r0 + (idx & 15);
-            const uint32_t hb = f32_to_bf16_bits(f[u]);
-            l_hi[rr * RS + r] = (uint16_t)hb;
-            l_lo[rr * RS + r] = (uint16_t)f32_to_bf16_bits(f[u] - bf16_bits_to_f32(hb));  // exact remainder
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < PI; ++u) {
-          const int idx = t + u * T::THREADS;
-          if ((T::BN * 16) % T::THREADS == 0 || idx < T::BN * 16) p_lds[(idx >> 4) * RS + r0 + (idx & 15)] = (uint16_t)pw[u];
-        }
-      }
-    }
-    __syncthreads();
+  for (int r = 0; r < D::ROUNDS; ++r) {
+    const int row = r * D::ROUND_ROWS + wave * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const bool is_a = row < T::BM;
+    const int src = is_a ? min(row, rows_a - 1) : min(row - T::BM, rows_b - 1);
+    c_base[r] = is_a ? qa + (size_t)m0 * kbytes : qw + (size_t)n0 * kbytes;
+    c_off[r] = (uint32_t)src * kbytes + 16u * (uint32_t)c;
   }
+  // scale dword of each round: LDS dword index d -> quad d / 8 (tile rows 4 quad ..), group d % 8
+  const uint8_t* s_base[D::SROUNDS];
+  uint32_t s_off[D::SROUNDS], s_stride[D::SROUNDS];
 #pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
-    }
-  if (LORA) {
-    for (int r0 = 0; r0 < rp; r0 += 16) {
-      bf16x8_t pv[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        pv[j] = *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * RS + r0 + 8 * h);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * FM * 32 + i * 32 + l32;
-        const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * RS + r0 + 8 * h);
-        const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * RS + r0 + 8 * h);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], llo, acc[i][j], 0, 0, 0);
-        }
-      }
-    }
+  for (int r = 0; r < D::SROUNDS; ++r) {
+    const int d = min((r * D::WAVES + wave) * 64 + lane, D::SDW - 1);
+    const int quad = d >> 3, g = d & 7;
+    const bool is_a = 4 * quad < T::BM;
+    const int row = is_a ? min(4 * quad, rows_a - 4) : min(4 * quad - T::BM, rows_b - 4);
+    s_base[r] = is_a ? sa + m0 : sw + n0;
+    s_stride[r] = is_a ? (uint32_t)M : (uint32_t)N;
+    s_off[r] = (uint32_t)g * s_stride[r] + (uint32_t)row;
   }
-  const bool n4 = (N & 3) == 0;
+
+
+  dma_issue<D>(lds + (0) * D::STAGE, wave, (uint32_t)(0) * (BK / 2), (size_t)(0) * (BK / 16), c_base, c_off,
+                 s_base, s_off, s_stride);
+  dma_issue<D>(lds + (1) * D::STAGE, wave, (uint32_t)(nkt > 1 ? 1 : 0) * (BK / 2), (size_t)(nkt > 1 ? 1 : 0) * (BK / 16), c_base, c_off,
+                 s_base, s_off, s_stride);
+  vm_wait_barrier<0>();
+
+  float16_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = mb + i * 32 + l32;
-    if (m >= M) continue;
-    uint16_t* yrow = y + (size_t)m * N;
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nb + j * 32 + 8 * q + 4 * h;
-        const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-        const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        if (n4) {
-          if (n < N) *reinterpret_cast<u32x2_t*>(yrow + n) = u32x2_t{p0, p1};
-        } else {
-          const uint16_t v[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // byte of the lane's row within a scale dword, as a v_perm selector: result byte 0 from the
+  // first dword, byte 1 from the second
+  const uint32_t psel = (uint32_t)(l32 & 3) | ((uint32_t)(4 + (l32 & 3)) << 8) | 0x0C0C0000u;
+  auto scales_of = [&](const uint8_t* cur, int row, uint32_t (&sp)[2]) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(cur + D::SCALE_OFF + (row >> 2) * 32 + 16 * h);
+    sp[0] = e4m3x2_to_h2bits(__builtin_amdgcn_perm(w[1], w[0], psel));
+    sp[1] = e4m3x2_to_h2bits(__builtin_amdgcn_perm(w[3], w[2], psel));
+  };
+
+  // Every iteration issues the same loads (the last two reload the final K-step into a slot
+  // nobody reads again), so every wave has the same count in flight at each wait.
+  int slot = 0;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int slot2 = slot == 0 ? 2 : slot - 1;  // (kt + 2) % 3: read in K-step kt - 1, now free
+    dma_issue<D>(lds + (slot2) * D::STAGE, wave, (uint32_t)(min(kt + 2, nkt - 1)) * (BK / 2), (size_t)(min(kt + 2, nkt - 1)) * (BK / 16), c_base, c_off,
+                 s_base, s_off, s_stride);
+    const uint8_t* cur = lds + slot * D::STAGE;
+    uint32_t sA[FM][2], sB[FN][2];
+    u32x4_t cA[2][FM], cB[2][FN];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) yrow[n + e] = v[e];
-        }
-      }
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * FM * 32 + i * 32 + l32;
+      const int sw4 = (row >> 1) & 3;
+      scales_of(cur, row, sA[i]);
+      cA[0][i] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h) ^ sw4));
+      cA[1][i] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h + 1) ^ sw4));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = T::BM + wn * FN * 32 + j * 32 + l32;
+      const int sw4 = (row >> 1) & 3;
+      scales_of(cur, row, sB[j]);
+      cB[0][j] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h) ^ sw4));
+      cB[1][j] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h + 1) ^ sw4));
+    }
+    mma_stage<FM, FN>(acc, sA, sB, cA, cB);
+    // K-step kt + 1's loads were issued before K-step kt + 2's: at most the latter are in flight
+    vm_wait_barrier<D::LOADS>();
+    slot = slot == 2 ? 0 : slot + 1;
   }
+  vm_wait_barrier<0>();  // the last reloads land before the epilogue reuses LDS
+
+  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
 }
 
 template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16>
@@ -459,9 +656,24 @@ hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* s
 }
 
 template <int WAVES_M, int WAVES_N, int FM, int FN>
-hipError_t launch_tile(int rb, bool vec16, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora,
+hipError_t launch_dma(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
+                      const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
+                      const uint16_t* wts, int M, int N, int K, int R, uint16_t* y) {
+  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
+  dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
+  dim3 block(T::THREADS);
+  if (rb > 0)
+    gemm_dma_kernel<WAVES_M, WAVES_N, FM, FN, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+  else
+    gemm_dma_kernel<WAVES_M, WAVES_N, FM, FN, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+  return hipGetLastError();
+}
+
+template <int WAVES_M, int WAVES_N, int FM, int FN>
+hipError_t launch_tile(bool dma, int rb, bool vec16, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora,
                        int parts, const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
                        const uint16_t* wts, int M, int N, int K, int R, uint16_t* y) {
+  if (dma) return launch_dma<WAVES_M, WAVES_N, FM, FN>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
   if (vec16)
     return launch_rb<WAVES_M, WAVES_N, FM, FN, true>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
   return launch_rb<WAVES_M, WAVES_N, FM, FN, false>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
@@ -505,6 +717,12 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
   auto wt = static_cast<const uint16_t*>(wtscale);
   auto yp = static_cast<uint16_t*>(y);
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R;
+  // The three-stage kernel with direct LDS loads needs whole 128-column K-steps and dword-aligned
+  // scale quads; W4A4_GEMM_PATH=stage forces the register-staged kernel.
+  const char* path = getenv("W4A4_GEMM_PATH");
+  const bool dma = (K % BK) == 0 && (M % 4) == 0 && (N % 4) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sw)) & 3) == 0 &&
+                   !(path && !strcmp(path, "stage"));
   // Pick the best-scoring variant; W4A4_GEMM_TILE (a variant name) forces one.
   const char* forced = getenv("W4A4_GEMM_TILE");
   int best = -1;
@@ -521,7 +739,7 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
     for (int i = 0; i < (int)(sizeof(kVariants) / sizeof(kVariants[0])); ++i)
       if (!strcmp(forced, kVariants[i].name)) best = i;
 #define W4A4_TILE_CASE(I, WM, WN, FM, FN) \
-  case I: return launch_tile<WM, WN, FM, FN>(rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+  case I: return launch_tile<WM, WN, FM, FN>(dma, rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
   switch (best) {
     W4A4_TILE_CASE(0, 2, 2, 4, 4)
     W4A4_TILE_CASE(1, 2, 2, 4, 3)
@@ -530,7 +748,7 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
     W4A4_TILE_CASE(4, 4, 2, 2, 4)
     W4A4_TILE_CASE(5, 2, 4, 4, 2)
     default:
-      return launch_tile<4, 2, 2, 3>(rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+      return launch_tile<4, 2, 2, 3>(dma, rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
   }
 #undef W4A4_TILE_CASE
 }

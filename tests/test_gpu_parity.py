@@ -140,6 +140,17 @@ def test_gemm_lowrank_parity(w4, M, N, K, R):
     _check_gemm(w4, lay)
 
 
+@pytest.mark.parametrize("path", ["stream", "regs"])
+@pytest.mark.parametrize("M,N,K,R", [(16, 600, 5120, 32), (1, 64, 512, 8), (13, 36, 8192, 64), (16, 100, 1024, 0),
+                                     (8, 200, 2560, 16), (12, 68, 3584, 32), (4, 40, 512, 64)])
+def test_skinny_paths(w4, M, N, K, R, path, monkeypatch):
+    """Both weight-streaming kernels (LDS-staged row streaming, and registers-only, forced through
+    W4A4_SKINNY_PATH) on shapes the streaming one accepts."""
+    monkeypatch.setenv("W4A4_SKINNY_PATH", path)
+    lay = synth.make_layer("tiny", seed=M * 3 + K, M=M, K=K, N=N, R=R, B=0, wcs="uniform")
+    _check_gemm(w4, lay)
+
+
 GEMM_VARIANTS = ["2x2x4x4", "2x2x4x3", "2x2x4x2", "2x2x2x2", "4x2x2x4", "2x4x4x2", "4x2x2x3"]
 
 

@@ -6,8 +6,10 @@
 // With a handful of rows every weight byte is used once, so the layer is bound by
 // streaming qweight/wscales from HBM.  Each workgroup owns 32 weight rows and all
 // of K; its 8 waves split K into contiguous runs of 128-column steps and stream
-// their weights straight into registers (two-step chunks, double-buffered, so
-// several chunks of loads are in flight per wave).  No LDS staging is used for
+// their weights straight into registers, issuing the loads of up to 8 steps
+// before decoding any, so one memory latency covers the wave's whole share.  The
+// epilogue operands (low-rank partial sums, proj_up, wcscales) are fetched before
+// the weights, so their latency overlaps the stream.  No LDS staging is used for
 // the weights.  Decoding is exact (E2M1 -> f16 convert, one f16 multiply by the
 // e4m3 scale) and the products run on v_mfma_f32_16x16x32_f16 with the weights
 // as the first operand, so a lane's accumulator holds 4 consecutive n of one m.
@@ -15,6 +17,7 @@
 // epilogue applies wcscales * wtscale and adds the rank-R correction in float32
 // (L from `parts` partial sums, added in order).
 #include <cstdlib>
+#include <cstring>
 
 #include "device_common.h"
 #include "w4a4.h"
@@ -26,7 +29,8 @@ namespace {
 
 constexpr int SK_WAVES = 8;
 constexpr int SK_BN = 32;      // weight rows per workgroup (two 16-row MFMA blocks)
-constexpr int SK_CHUNK = 2;    // K-steps per prefetch chunk
+constexpr int SK_MAXPARTS = 8;  // low-rank partial sums whose loads are issued together
+constexpr int SK_BATCH = 5;    // K-steps whose loads are issued together
 
 template <int MB>
 struct SkinnyStep {
@@ -119,7 +123,36 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(
   const int per_wave = (nsteps + SK_WAVES - 1) / SK_WAVES;
   const int s_begin = wave * per_wave;
   const int s_end = min(s_begin + per_wave, nsteps);
-  const int nchunks = (max(s_end - s_begin, 0) + SK_CHUNK - 1) / SK_CHUNK;
+
+  // ---- epilogue operands first: their loads overlap the weight stream -------------------
+  constexpr int LPT = (MR * W4A4_MAX_RANK + 64 * SK_WAVES - 1) / (64 * SK_WAVES);
+  constexpr int PPT = (SK_BN * W4A4_MAX_RANK + 64 * SK_WAVES - 1) / (64 * SK_WAVES);
+  float lsum[LORA ? LPT : 1];
+  uint32_t pval[LORA ? PPT : 1];
+  uint32_t cval = 0u;
+  if (t < SK_BN) cval = wcs[min(n0 + t, N - 1)];
+  if (LORA) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int i = t + u * 64 * SK_WAVES;  // (m, r) = (i / R, i % R)
+      const int m = min(i / max(R, 1), M - 1), r = i % max(R, 1);
+      const size_t at = (size_t)m * R + r;
+      float v[SK_MAXPARTS];
+#pragma unroll
+      for (int p = 0; p < SK_MAXPARTS; ++p) v[p] = lora[(size_t)min(p, parts - 1) * M * R + at];
+      float sum = 0.0f;  // the parts in order; the spare terms add +0 and change nothing
+#pragma unroll
+      for (int p = 0; p < SK_MAXPARTS; ++p) sum += p < parts ? v[p] : 0.0f;
+      for (int p = SK_MAXPARTS; p < parts; ++p) sum += lora[(size_t)p * M * R + at];
+      lsum[u] = sum;
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = t + u * 64 * SK_WAVES;
+      const int n = min(n0 + i / max(R, 1), N - 1), r = i % max(R, 1);
+      pval[u] = pu[(size_t)n * R + r];
+    }
+  }
 
   float4_t acc[MB][2];
 #pragma unroll
@@ -127,26 +160,14 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[mb][b] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  SkinnyStep<MB> buf0[SK_CHUNK], buf1[SK_CHUNK];
-  auto load_chunk = [&](SkinnyStep<MB>(&dst)[SK_CHUNK], int c) {
+  for (int s0 = s_begin; s0 < s_end; s0 += SK_BATCH) {
+    SkinnyStep<MB> st[SK_BATCH];
 #pragma unroll
-    for (int i = 0; i < SK_CHUNK; ++i) {
-      const int s = s_begin + c * SK_CHUNK + i;
-      skinny_load<MB, VEC16>(dst[i], s, s < s_end, qa, sa, qw, sw, M, N, kbytes, groups, n0, r16, j);
-    }
-  };
-  auto compute_chunk = [&](const SkinnyStep<MB>(&src)[SK_CHUNK]) {
+    for (int i = 0; i < SK_BATCH; ++i)
+      skinny_load<MB, VEC16>(st[i], s0 + i, s0 + i < s_end, qa, sa, qw, sw, M, N, kbytes, groups, n0, r16, j);
 #pragma unroll
-    for (int i = 0; i < SK_CHUNK; ++i) skinny_compute<MB>(src[i], acc);
-  };
-  if (nchunks > 0) load_chunk(buf0, 0);
-  for (int c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks) load_chunk(buf1, c + 1);
-    compute_chunk(buf0);
-    if (c + 1 < nchunks) {
-      if (c + 2 < nchunks) load_chunk(buf0, c + 2);
-      compute_chunk(buf1);
-    }
+    for (int i = 0; i < SK_BATCH; ++i)
+      if (s0 + i < s_end) skinny_compute<MB>(st[i], acc);  // wave-uniform
   }
 
   // per-wave partials -> LDS: lane holds m = 16mb + lane%16, n = 16b + 4j + e
@@ -156,23 +177,22 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[wave][16 * mb + r16][16 * b + 4 * j + e] = acc[mb][b][e];
+  __shared__ float c_lds[SK_BN];
+  if (t < SK_BN) c_lds[t] = bf16_bits_to_f32(cval) * bf16_bits_to_f32(wts[0]);
   if (LORA) {
     // L[m, r] = sum of the parts, in order; proj_up rows of this workgroup as float32
-    for (int i = t; i < MR * R; i += 64 * SK_WAVES) {
-      const int m = i / R, r = i % R;
-      float s = 0.0f;
-      if (m < M)
-        for (int p = 0; p < parts; ++p) s += lora[(size_t)p * M * R + (size_t)m * R + r];
-      l_lds[m * W4A4_MAX_RANK + r] = s;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int i = t + u * 64 * SK_WAVES;
+      if (i < MR * R) l_lds[(i / R) * W4A4_MAX_RANK + i % R] = lsum[u];
     }
-    for (int i = t; i < SK_BN * R; i += 64 * SK_WAVES) {
-      const int n = i / R, r = i % R;
-      const int nn = min(n0 + n, N - 1);
-      p_lds[n * (W4A4_MAX_RANK + 1) + r] = bf16_bits_to_f32(pu[(size_t)nn * R + r]);
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = t + u * 64 * SK_WAVES;
+      if (i < SK_BN * R) p_lds[(i / R) * (W4A4_MAX_RANK + 1) + i % R] = bf16_bits_to_f32(pval[u]);
     }
   }
   __syncthreads();
-  const float ts = bf16_bits_to_f32(wts[0]);
   for (int i = t; i < MR * SK_BN; i += 64 * SK_WAVES) {
     const int m = i / SK_BN, n = i % SK_BN;
     float s = 0.0f;
@@ -180,13 +200,186 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(
     for (int w = 0; w < SK_WAVES; ++w) s += red[w][m][n];
     const int gn = n0 + n;
     if (m >= M || gn >= N) continue;
-    float v = s * (bf16_bits_to_f32(wcs[gn]) * ts);
+    float v = s * c_lds[n];
     if (LORA) {
       float l = 0.0f;
       for (int r = 0; r < R; ++r) l = __builtin_fmaf(l_lds[m * W4A4_MAX_RANK + r], p_lds[n * (W4A4_MAX_RANK + 1) + r], l);
       v += l;
     }
     y[(size_t)m * N + gn] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+// ---- streaming variant for M <= 16 (a multiple of 4), K <= 5120 (a multiple of 512) -----
+// The loads follow the layout of memory: for each 256-byte chunk of a row (512 K-columns),
+// thread t reads 16 bytes of weight row t / 16 at byte 16 (t % 16) (32 runs of 256 contiguous
+// bytes per instruction) and 8 bytes of activation row t / 32 at byte 8 (t % 32); the first
+// threads also read the chunk's wscales and ascales as dwords (4 rows of one group).  A
+// workgroup issues the loads of all its chunks (its whole share of K) before any compute.  The
+// chunks then pass through LDS, five at a time, to reach the MFMA layout: wave w computes a
+// chunk's K-columns 64w .. 64w + 63; lane (row i = lane % 16, kg = lane / 16) takes the 8
+// bytes at 32w + 8kg (16 codes, two MFMA sub-steps, one 16-group 4w + kg) of its row, for the
+// activations and for both 16-row weight blocks.
+constexpr int SS_CH = 256;                // bytes of a row per chunk (512 K-columns)
+constexpr int SS_ROW = SS_CH + 16;        // LDS bytes per row of a chunk (16 bytes of padding)
+constexpr int SS_MAXC = 10;               // chunks of K (K <= 5120), loads all issued up front
+constexpr int SS_PHASE = 5;               // chunks staged in LDS per barrier
+constexpr int SS_MAXPARTS = 8;            // low-rank partial sums the epilogue adds
+constexpr int SS_W = 0;                               // slot layout: weight rows
+constexpr int SS_S = SS_W + SK_BN * SS_ROW;           // wscales [group][32 rows]
+constexpr int SS_A = SS_S + 32 * SK_BN;               // activation rows
+constexpr int SS_AS = SS_A + 16 * SS_ROW;             // ascales [group][16 rows]
+constexpr int SS_SLOT = SS_AS + 32 * 16;
+constexpr int SS_LDS = SS_PHASE * SS_SLOT;
+
+template <bool LORA>
+__global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_stream_kernel(
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
+    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
+    uint16_t* __restrict__ y) {
+  constexpr int MR = 16;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SS_LDS];
+  // after the chunk loop the same bytes hold the reduction and the epilogue operands
+  float (*red)[MR][SK_BN] = reinterpret_cast<float (*)[MR][SK_BN]>(smem);
+  float* l_lds = reinterpret_cast<float*>(smem + SK_WAVES * MR * SK_BN * 4);
+  float* p_lds = l_lds + MR * W4A4_MAX_RANK;
+  float* c_lds = p_lds + SK_BN * (W4A4_MAX_RANK + 1);
+  static_assert(SK_WAVES * MR * SK_BN * 4 + (MR * W4A4_MAX_RANK + SK_BN * (W4A4_MAX_RANK + 1) + SK_BN) * 4 <= SS_LDS,
+                "epilogue fits the staging area");
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int n0 = blockIdx.x * SK_BN;
+  const int kbytes = K / 2;
+  const int nc = kbytes / SS_CH;  // 1 .. SS_MAXC
+
+  // ---- every load of the workgroup's share, up front (clamped past the last chunk) ------
+  const uint8_t* wsrc = qw + (size_t)min(n0 + (t >> 4), N - 1) * kbytes + 16 * (t & 15);
+  const uint8_t* asrc = qa + (size_t)min(t >> 5, M - 1) * kbytes + 8 * (t & 31);
+  const int sg = (t >> 3) & 31, sq = t & 7;  // wscales dword of threads < 256
+  const uint8_t* ssrc = sw + (size_t)sg * N + min(n0 + 4 * sq, N - 4);
+  const int ag = (t >> 2) & 31, aq = t & 3;  // ascales dword of threads < 128
+  const uint8_t* assrc = sa + (size_t)ag * M + min(4 * aq, M - 4);
+  u32x4_t wr[SS_MAXC];
+  u32x2_t ar[SS_MAXC];
+  uint32_t sr[SS_MAXC], asr[SS_MAXC];
+#pragma unroll
+  for (int i = 0; i < SS_MAXC; ++i) {
+    const int c = min(i, nc - 1);
+    wr[i] = *reinterpret_cast<const u32x4_t*>(wsrc + (size_t)c * SS_CH);
+    ar[i] = *reinterpret_cast<const u32x2_t*>(asrc + (size_t)c * SS_CH);
+  }
+  if (t < 256) {
+#pragma unroll
+    for (int i = 0; i < SS_MAXC; ++i) sr[i] = *reinterpret_cast<const uint32_t*>(ssrc + (size_t)min(i, nc - 1) * 32 * N);
+  }
+  if (t < 128) {
+#pragma unroll
+    for (int i = 0; i < SS_MAXC; ++i) asr[i] = *reinterpret_cast<const uint32_t*>(assrc + (size_t)min(i, nc - 1) * 32 * M);
+  }
+
+  float4_t acc[2];
+  acc[0] = float4_t{0.f, 0.f, 0.f, 0.f};
+  acc[1] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const int a_group = 4 * wave + kg;  // 16-group of the lane within a chunk
+#pragma unroll
+  for (int ph = 0; ph < SS_MAXC; ph += SS_PHASE) {
+    if (ph >= nc) continue;  // workgroup-uniform
+    if (ph > 0) __syncthreads();  // every wave is done with the previous phase's slots
+#pragma unroll
+    for (int i = ph; i < ph + SS_PHASE; ++i) {
+      uint8_t* slot = smem + (i - ph) * SS_SLOT;
+      *reinterpret_cast<u32x4_t*>(slot + SS_W + (t >> 4) * SS_ROW + 16 * (t & 15)) = wr[i];
+      *reinterpret_cast<u32x2_t*>(slot + SS_A + (t >> 5) * SS_ROW + 8 * (t & 31)) = ar[i];
+      if (t < 256) *reinterpret_cast<uint32_t*>(slot + SS_S + sg * SK_BN + 4 * sq) = sr[i];
+      if (t < 128) *reinterpret_cast<uint32_t*>(slot + SS_AS + ag * 16 + 4 * aq) = asr[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = ph; i < ph + SS_PHASE; ++i) {
+      if (i >= nc) continue;  // workgroup-uniform
+      const uint8_t* slot = smem + (i - ph) * SS_SLOT;
+      const u32x2_t ac = *reinterpret_cast<const u32x2_t*>(slot + SS_A + r16 * SS_ROW + 32 * wave + 8 * kg);
+      const uint32_t asb = slot[SS_AS + a_group * 16 + r16];
+      const uint32_t ash = e4m3x2_to_h2bits(asb | (asb << 8));
+      const half8_t a0 = decode8(ac[0], scale_pair(ash, 0));
+      const half8_t a1 = decode8(ac[1], scale_pair(ash, 0));
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int row = 16 * b + r16;
+        const u32x2_t wc = *reinterpret_cast<const u32x2_t*>(slot + SS_W + row * SS_ROW + 32 * wave + 8 * kg);
+        const uint32_t wsb = slot[SS_S + a_group * SK_BN + row];
+        const uint32_t wsh = e4m3x2_to_h2bits(wsb | (wsb << 8));
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode8(wc[0], scale_pair(wsh, 0)), a0, acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode8(wc[1], scale_pair(wsh, 0)), a1, acc[b], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue operands (fetched after the stream: holding them during it would spill) ----
+  constexpr int LPT = (MR * W4A4_MAX_RANK + 64 * SK_WAVES - 1) / (64 * SK_WAVES);
+  constexpr int PPT = (SK_BN * W4A4_MAX_RANK + 64 * SK_WAVES - 1) / (64 * SK_WAVES);
+  float lsum[LORA ? LPT : 1];
+  uint32_t pval[LORA ? PPT : 1];
+  const uint32_t cval = wcs[min(n0 + (t % SK_BN), N - 1)];
+  if (LORA) {
+    lsum[LPT - 1] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      if (u > 0 && MR * R <= u * 64 * SK_WAVES) continue;  // uniform: no rows of R ranks left
+      const int i = t + u * 64 * SK_WAVES;
+      const size_t at = (size_t)min(i / R, M - 1) * R + i % R;
+      float v[SS_MAXPARTS];
+#pragma unroll
+      for (int p = 0; p < SS_MAXPARTS; ++p) v[p] = lora[(size_t)min(p, parts - 1) * M * R + at];
+      float sum = 0.0f;  // the parts in order; the spare terms add +0 and change nothing
+#pragma unroll
+      for (int p = 0; p < SS_MAXPARTS; ++p) sum += p < parts ? v[p] : 0.0f;
+      lsum[u] = sum;
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = t + u * 64 * SK_WAVES;
+      pval[u] = pu[(size_t)min(n0 + i / R, N - 1) * R + i % R];
+    }
+  }
+  __syncthreads();  // the staging area is reused below
+
+  // per-wave partials -> LDS: lane holds m = lane%16, n = 16b + 4 kg + e
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][r16][16 * b + 4 * kg + e] = acc[b][e];
+  if (t < SK_BN) c_lds[t] = bf16_bits_to_f32(cval) * bf16_bits_to_f32(wts[0]);
+  if (LORA) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int i = t + u * 64 * SK_WAVES;
+      if (i < MR * R) l_lds[(i / R) * W4A4_MAX_RANK + i % R] = lsum[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = t + u * 64 * SK_WAVES;
+      if (i < SK_BN * R) p_lds[(i / R) * (W4A4_MAX_RANK + 1) + i % R] = bf16_bits_to_f32(pval[u]);
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < MR * SK_BN; i += 64 * SK_WAVES) {
+    const int mm = i / SK_BN, n = i % SK_BN;
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < SK_WAVES; ++w) s += red[w][mm][n];
+    const int gn = n0 + n;
+    if (mm >= M || gn >= N) continue;
+    float v = s * c_lds[n];
+    if (LORA) {
+      float l = 0.0f;
+      for (int r = 0; r < R; ++r) l = __builtin_fmaf(l_lds[mm * W4A4_MAX_RANK + r], p_lds[n * (W4A4_MAX_RANK + 1) + r], l);
+      v += l;
+    }
+    y[(size_t)mm * N + gn] = (uint16_t)f32_to_bf16_bits(v);
   }
 }
 
@@ -218,6 +411,19 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
   auto yp = static_cast<uint16_t*>(y);
   const bool vec16 = (K % 32) == 0, lo = R > 0;
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R;
+  const bool streamed = M <= 16 && (M % 4) == 0 && (K % (2 * SS_CH)) == 0 && K <= 2 * SS_CH * SS_MAXC &&
+                        (N % 4) == 0 && ((reinterpret_cast<uintptr_t>(sa) & 3) == 0) &&
+                        lora_parts <= SS_MAXPARTS &&
+                      ((reinterpret_cast<uintptr_t>(sw) | reinterpret_cast<uintptr_t>(qa)) & 7) == 0 &&
+                      !(getenv("W4A4_SKINNY_PATH") && !strcmp(getenv("W4A4_SKINNY_PATH"), "regs"));
+  if (streamed) {
+    dim3 grid((unsigned)((N + SK_BN - 1) / SK_BN)), block(64 * SK_WAVES);
+    if (lo)
+      gemm_skinny_stream_kernel<true><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+    else
+      gemm_skinny_stream_kernel<false><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+    return hipGetLastError();
+  }
   if (M <= 16) {
     if (vec16) return launch_mb<1, true>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
     return launch_mb<1, false>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);

@@ -131,6 +131,8 @@ GEMM_CASES = [
     (32, 129, 48, 5),
     (31, 64, 4096, 64),
     (2, 33, 16, 0),
+    # more than 8192 columns: the 64-row wide kernel (rank padded to 64; M not a multiple of 4)
+    (12, 8194, 1536, 40),
 ]
 
 
@@ -140,12 +142,12 @@ def test_gemm_lowrank_parity(w4, M, N, K, R):
     _check_gemm(w4, lay)
 
 
-@pytest.mark.parametrize("path", ["stream", "regs"])
+@pytest.mark.parametrize("path", ["wide", "stream", "regs"])
 @pytest.mark.parametrize("M,N,K,R", [(16, 600, 5120, 32), (1, 64, 512, 8), (13, 36, 8192, 64), (16, 100, 1024, 0),
-                                     (8, 200, 2560, 16), (12, 68, 3584, 32), (4, 40, 512, 64)])
+                                     (8, 200, 2560, 16), (12, 68, 3584, 32), (4, 40, 512, 64), (16, 130, 1024, 33)])
 def test_skinny_paths(w4, M, N, K, R, path, monkeypatch):
-    """Both weight-streaming kernels (LDS-staged row streaming, and registers-only, forced through
-    W4A4_SKINNY_PATH) on shapes the streaming one accepts."""
+    """Each weight-streaming kernel (64-row wide, 32-row LDS-staged, registers-only), forced
+    through W4A4_SKINNY_PATH; shapes a variant does not accept fall back to the next one."""
     monkeypatch.setenv("W4A4_SKINNY_PATH", path)
     lay = synth.make_layer("tiny", seed=M * 3 + K, M=M, K=K, N=N, R=R, B=0, wcs="uniform")
     _check_gemm(w4, lay)
@@ -168,7 +170,8 @@ def test_gemm_every_tile_variant(w4, variant, path, monkeypatch):
 @pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 0), (37, 70, 256, 32, 128), (3, 40, 48, 3, 16),
                                        (150, 260, 512, 64, 64),
                                        # small batches: K split across quantizer workgroups (partial low-rank sums)
-                                       (16, 200, 4096, 32, 0), (9, 100, 8192, 16, 128), (32, 64, 1024, 64, 32)])
+                                       (16, 200, 4096, 32, 0), (9, 100, 8192, 16, 128), (32, 64, 1024, 64, 32),
+                                       (16, 8200, 2048, 32, 0)])
 def test_linear_parity(w4, M, N, K, R, B):
     import torch
     lay = synth.make_layer("tiny", seed=11 + M, M=M, K=K, N=N, R=R, B=B, wcs="uniform")

@@ -4,18 +4,20 @@
 // GEMM then the BF16 rank correction):
 //   y[m,n] = bf16( sum_k A[m,k] W[n,k] * wcscales[n] * wtscale + sum_r L[m,r] proj_up[n,r] )
 // With a handful of rows every weight byte is used once, so the layer is bound by
-// streaming qweight/wscales from HBM.  Each workgroup owns 32 weight rows and all
-// of K; its 8 waves split K into contiguous runs of 128-column steps and stream
-// their weights straight into registers, issuing the loads of up to 8 steps
-// before decoding any, so one memory latency covers the wave's whole share.  The
-// epilogue operands (low-rank partial sums, proj_up, wcscales) are fetched before
-// the weights, so their latency overlaps the stream.  No LDS staging is used for
-// the weights.  Decoding is exact (E2M1 -> f16 convert, one f16 multiply by the
-// e4m3 scale) and the products run on v_mfma_f32_16x16x32_f16 with the weights
-// as the first operand, so a lane's accumulator holds 4 consecutive n of one m.
-// The 8 per-wave partial sums are added in a fixed order through LDS; the
-// epilogue applies wcscales * wtscale and adds the rank-R correction in float32
-// (L from `parts` partial sums, added in order).
+// streaming qweight/wscales from HBM.  Decoding is exact (E2M1 -> f16 convert, one f16
+// multiply by the e4m3 scale) and the products run on v_mfma_f32_16x16x32_f16 with the
+// weights as the first operand, so a lane's accumulator holds 4 consecutive n of one m.
+// Three variants:
+//   * wide (M <= 16, K <= 5120, more than 8192 columns): 64 weight rows per 1024-thread
+//     workgroup, chunks of 512 K-columns staged through LDS two chunks ahead of the compute,
+//     each code decoded once per workgroup;
+//   * stream (M <= 16, K <= 5120, fewer columns): 32 rows per 512-thread workgroup, every
+//     load of the workgroup's share issued up front, staged through LDS in two phases;
+//   * registers (any K, M <= 32): 32 rows per workgroup, 8 waves split K into contiguous
+//     runs of 128-column steps loaded straight into registers in the MFMA layout.
+// The per-wave partial sums are added in a fixed order through LDS; the epilogue applies
+// wcscales * wtscale and adds the rank-R correction in float32 (L from `parts` partial sums,
+// added in order).
 #include <cstdlib>
 #include <cstring>
 
@@ -383,6 +385,188 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_stream_kernel(
   }
 }
 
+// ---- wide variant for M <= 16, K <= 5120 (a multiple of 512) and many columns --------------
+// One 1024-thread workgroup per 64 weight rows (four 16-row MFMA blocks) and all of K.  Chunks
+// of 512 K-columns pass through LDS: per chunk, thread t loads 16 bytes of weight row t / 16,
+// 4 bytes of activation row t / 64, two wscales bytes (group t / 32) and one ascales byte; the
+// scales are widened to f16 pairs as they are stored.  Wave w owns the chunk's K-columns
+// 32w .. 32w + 31 for all four blocks, so each activation code and each weight code of the
+// tile is decoded once; lane (i = lane % 16, kg = lane / 16) takes the 8 codes at byte
+// 16w + 4kg of its rows.  Loads run SW_AHEAD chunks ahead of the compute: a deeper prefetch,
+// or issuing every chunk up front, delays the first chunk (the memory system serves a
+// workgroup's outstanding requests together) and measured slower.  Tiles are numbered so
+// that consecutive tiles run on one XCD (workgroups go to the 8 XCDs in turn) and share the
+// L2 lines of wscales.  The 16 per-wave partial sums meet in LDS in a fixed order; the rank-R
+// term runs on the matrix cores (L split into bf16 hi + lo parts) and is added before the
+// single rounding to bf16.
+constexpr int SW_WAVES = 16;
+constexpr int SW_BN = 64;                            // weight rows per workgroup
+constexpr int SW_AHEAD = 2;                          // chunks in flight ahead of the compute
+constexpr int SW_SSTR = 80;                          // dwords per group row of staged wscales
+constexpr int SW_W = 0;                              // slot: weight rows (SS_ROW bytes each)
+constexpr int SW_A = SW_W + SW_BN * SS_ROW;          //       activation rows
+constexpr int SW_S = SW_A + 16 * SS_ROW;             //       wscales as f16 pairs [32 groups][SW_SSTR]
+constexpr int SW_AS = SW_S + 32 * SW_SSTR * 4;       //       ascales as f16 pairs [32 groups][16 rows]
+constexpr int SW_SLOT = SW_AS + 32 * 16 * 4;
+constexpr int SW_RED = 68;                           // floats per row of the reduction area
+constexpr int SW_REDB = (SW_WAVES + 1) * 16 * SW_RED * 4;
+constexpr int SW_EPI = 2 * SW_SLOT > SW_REDB ? 2 * SW_SLOT : SW_REDB;
+constexpr int SW_RS = W4A4_MAX_RANK + 8;             // bf16 per staged rank row (144-byte rows)
+constexpr int SW_LHI = SW_EPI;
+constexpr int SW_LLO = SW_LHI + 16 * SW_RS * 2;
+constexpr int SW_P = SW_LLO + 16 * SW_RS * 2;
+constexpr int SW_C = SW_P + SW_BN * SW_RS * 2;
+constexpr int SW_TRASH = SW_C + SW_BN * 4;           // target of lanes with nothing to store
+constexpr int SW_LDS = SW_TRASH + 16;
+static_assert(SW_LDS <= 160 * 1024, "LDS of one CU");
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Tile of workgroup b when workgroups are dispatched to the 8 XCDs in turn: XCD x runs a
+// contiguous range of tiles.
+__device__ __forceinline__ int xcd_tile(int b, int G) {
+  const int q = G / 8, r = G % 8, x = b % 8, l = b / 8;
+  return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+}
+
+template <bool LORA, int RP>
+__global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_wide_kernel(
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
+    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
+    uint16_t* __restrict__ y) {
+  static_assert(!LORA || RP == 32 || RP == 64, "rank padded to one or two MFMA steps");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SW_LDS];
+  uint16_t* l_hi = reinterpret_cast<uint16_t*>(smem + SW_LHI);
+  uint16_t* l_lo = reinterpret_cast<uint16_t*>(smem + SW_LLO);
+  uint16_t* p_lds = reinterpret_cast<uint16_t*>(smem + SW_P);
+  float* c_lds = reinterpret_cast<float*>(smem + SW_C);
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int n0 = xcd_tile(blockIdx.x, gridDim.x) * SW_BN;
+  const int kbytes = K / 2;
+  const int nc = kbytes / SS_CH;  // 1 .. SS_MAXC
+
+  // ---- epilogue operands first: the oldest loads, complete before the first chunk is used ----
+  // Every load here and below is unconditional (indices clamped), so none is moved past its use.
+  constexpr int RPP = RP > 0 ? RP : 1;
+  constexpr int PPT = LORA ? SW_BN * RP / (64 * SW_WAVES) : 1;
+  const uint32_t cval = wcs[min(n0 + (t & 63), N - 1)];
+  const uint32_t tsv = wts[0];
+  const int lm = t / RPP, lr = t % RPP;  // the (m, r) element of L this thread stages
+  float lv[SS_MAXPARTS];
+  uint32_t pval[PPT];
+  if (LORA) {
+    const int at = min(min(lm, M - 1) * R + min(lr, R - 1), M * R - 1);
+#pragma unroll
+    for (int p = 0; p < SS_MAXPARTS; ++p) lv[p] = lora[(size_t)min(p, parts - 1) * M * R + at];
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = t + u * 64 * SW_WAVES;
+      pval[u] = pu[(size_t)min(n0 + i / RPP, N - 1) * R + min(i % RPP, R - 1)];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint8_t* wsrc = qw + (size_t)min(n0 + (t >> 4), N - 1) * kbytes + 16 * (t & 15);
+  const uint8_t* asrc = qa + (size_t)min(t >> 6, M - 1) * kbytes + 4 * (t & 63);
+  const uint8_t* ssrc = sw + (size_t)(t >> 5) * N + min(n0 + 2 * (t & 31), N - 2);
+  const uint8_t* assrc = sa + (size_t)((t & 511) >> 4) * M + min(t & 15, M - 1);
+  u32x4_t wr[SS_MAXC];
+  uint32_t ar[SS_MAXC], sr[SS_MAXC], asr[SS_MAXC];
+// chunk j's loads (chunks past the last reload it); the scheduling barrier keeps chunks in order
+#define W4A4_SW_ISSUE(j)                                                              \
+  do {                                                                                \
+    const int c_ = min((j), nc - 1);                                                  \
+    wr[(j)] = *reinterpret_cast<const u32x4_t*>(wsrc + (size_t)c_ * SS_CH);           \
+    ar[(j)] = *reinterpret_cast<const uint32_t*>(asrc + (size_t)c_ * SS_CH);          \
+    sr[(j)] = *reinterpret_cast<const uint16_t*>(ssrc + (size_t)c_ * 32 * N);         \
+    asr[(j)] = assrc[(size_t)c_ * 32 * M];                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+  } while (0)
+#pragma unroll
+  for (int j = 0; j < SW_AHEAD; ++j) W4A4_SW_ISSUE(j);
+
+  c_lds[t & 63] = bf16_bits_to_f32(cval) * bf16_bits_to_f32(tsv);  // repeated lanes store the same value
+  if (LORA) {
+    // L[m, r] = sum of the parts in order (zero outside M x R), as bf16 hi + lo
+    float sum = 0.0f;
+#pragma unroll
+    for (int p = 0; p < SS_MAXPARTS; ++p) sum += p < parts ? lv[p] : 0.0f;
+    sum = (lm < M && lr < R) ? sum : 0.0f;
+    const uint32_t hb = f32_to_bf16_bits(sum);
+    const uint32_t lb = f32_to_bf16_bits(sum - bf16_bits_to_f32(hb));  // exact remainder, rounded
+    const bool staged = t < 16 * RP;
+    *(staged ? l_hi + lm * SW_RS + lr : reinterpret_cast<uint16_t*>(smem + SW_TRASH)) = (uint16_t)hb;
+    *(staged ? l_lo + lm * SW_RS + lr : reinterpret_cast<uint16_t*>(smem + SW_TRASH + 2)) = (uint16_t)lb;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = t + u * 64 * SW_WAVES;
+      p_lds[(i / RPP) * SW_RS + i % RPP] = (i % RPP) < R ? (uint16_t)pval[u] : (uint16_t)0;
+    }
+  }
+
+  float4_t acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const int kb = 16 * wave + 4 * kg;   // byte of the lane's 8 codes within a chunk row
+  const int g = 2 * wave + (kg >> 1);  // their 16-group within the chunk
+#pragma unroll
+  for (int i = 0; i < SS_MAXC; ++i) {
+    if (i + SW_AHEAD < SS_MAXC) W4A4_SW_ISSUE(i + SW_AHEAD);
+    // every chunk is staged, also past the last one, so the loads stay where they were issued
+    uint8_t* slot = smem + (i & 1) * SW_SLOT;
+    *reinterpret_cast<u32x4_t*>(slot + SW_W + (t >> 4) * SS_ROW + 16 * (t & 15)) = wr[i];
+    *reinterpret_cast<uint32_t*>(slot + SW_A + (t >> 6) * SS_ROW + 4 * (t & 63)) = ar[i];
+    *reinterpret_cast<u32x2_t*>(slot + SW_S + (t >> 5) * SW_SSTR * 4 + 8 * (t & 31)) =
+        u32x2_t{e4m3_to_h2bits(sr[i] & 0xFFu), e4m3_to_h2bits((sr[i] >> 8) & 0xFFu)};
+    *reinterpret_cast<uint32_t*>(slot + SW_AS + (t & 511) * 4) = e4m3_to_h2bits(asr[i]);  // halves agree
+    lds_barrier();  // also: every wave is done with the chunk this slot held two steps ago
+    if (i >= nc) continue;  // workgroup-uniform
+    const uint32_t a4 = *reinterpret_cast<const uint32_t*>(slot + SW_A + r16 * SS_ROW + kb);
+    const uint32_t as2 = *reinterpret_cast<const uint32_t*>(slot + SW_AS + (g * 16 + r16) * 4);
+    const half8_t av = decode8(a4, __builtin_bit_cast(half2_t, as2));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t w4 = *reinterpret_cast<const uint32_t*>(slot + SW_W + (16 * b + r16) * SS_ROW + kb);
+      const uint32_t ws2 = *reinterpret_cast<const uint32_t*>(slot + SW_S + (g * SW_SSTR + 16 * b + r16) * 4);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode8(w4, __builtin_bit_cast(half2_t, ws2)), av, acc[b], 0, 0,
+                                                      0);
+    }
+  }
+#undef W4A4_SW_ISSUE
+  lds_barrier();  // the slots are free: the reduction reuses them
+
+  // partials -> LDS: lane holds m = lane % 16, n = 16b + 4kg + e; rows 16 * 16 .. hold the
+  // rank-R term (waves 0..3, one 16-column block each)
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    *reinterpret_cast<float4_t*>(red + (wave * 16 + r16) * SW_RED + 16 * b + 4 * kg) = acc[b];
+  if (LORA && wave < 4) {
+    float4_t la = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r0 = 0; r0 < RP; r0 += 32) {
+      const bf16x8_t pv = *reinterpret_cast<const bf16x8_t*>(p_lds + (16 * wave + r16) * SW_RS + r0 + 8 * kg);
+      const bf16x8_t lh = *reinterpret_cast<const bf16x8_t*>(l_hi + r16 * SW_RS + r0 + 8 * kg);
+      const bf16x8_t ll = *reinterpret_cast<const bf16x8_t*>(l_lo + r16 * SW_RS + r0 + 8 * kg);
+      la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv, lh, la, 0, 0, 0);
+      la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv, ll, la, 0, 0, 0);
+    }
+    *reinterpret_cast<float4_t*>(red + (SW_WAVES * 16 + r16) * SW_RED + 16 * wave + 4 * kg) = la;
+  }
+  lds_barrier();
+  const int m = t >> 6, n = t & 63;
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < SW_WAVES; ++w) s += red[(w * 16 + m) * SW_RED + n];
+  float v = s * c_lds[n];
+  if (LORA) v += red[(SW_WAVES * 16 + m) * SW_RED + n];
+  if (m < M && n0 + n < N) y[(size_t)m * N + n0 + n] = (uint16_t)f32_to_bf16_bits(v);
+}
+
 template <int MB, bool VEC16>
 hipError_t launch_mb(bool lora_on, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                      const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs, const uint16_t* wts,
@@ -411,11 +595,27 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
   auto yp = static_cast<uint16_t*>(y);
   const bool vec16 = (K % 32) == 0, lo = R > 0;
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R;
+  // W4A4_SKINNY_PATH=wide|stream|regs picks a variant (for tests); by default the wide kernel
+  // serves more than 8192 columns, where the 32-row variants would need two workgroups per CU
+  const char* path = getenv("W4A4_SKINNY_PATH");
   const bool streamed = M <= 16 && (M % 4) == 0 && (K % (2 * SS_CH)) == 0 && K <= 2 * SS_CH * SS_MAXC &&
                         (N % 4) == 0 && ((reinterpret_cast<uintptr_t>(sa) & 3) == 0) &&
                         lora_parts <= SS_MAXPARTS &&
-                      ((reinterpret_cast<uintptr_t>(sw) | reinterpret_cast<uintptr_t>(qa)) & 7) == 0 &&
-                      !(getenv("W4A4_SKINNY_PATH") && !strcmp(getenv("W4A4_SKINNY_PATH"), "regs"));
+                        ((reinterpret_cast<uintptr_t>(sw) | reinterpret_cast<uintptr_t>(qa)) & 7) == 0 &&
+                        !(path && !strcmp(path, "regs"));
+  const bool wide = M <= 16 && (K % (2 * SS_CH)) == 0 && K <= 2 * SS_CH * SS_MAXC && (N % 2) == 0 &&
+                    ((reinterpret_cast<uintptr_t>(sw) & 1) == 0) && lora_parts <= SS_MAXPARTS &&
+                    (path ? !strcmp(path, "wide") : N > 8192);
+  if (wide) {
+    dim3 grid((unsigned)((N + SW_BN - 1) / SW_BN)), block(64 * SW_WAVES);
+    if (!lo)
+      gemm_skinny_wide_kernel<false, 0><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+    else if (r <= 32)
+      gemm_skinny_wide_kernel<true, 32><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+    else
+      gemm_skinny_wide_kernel<true, 64><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+    return hipGetLastError();
+  }
   if (streamed) {
     dim3 grid((unsigned)((N + SK_BN - 1) / SK_BN)), block(64 * SK_WAVES);
     if (lo)

@@ -429,7 +429,14 @@ __device__ __forceinline__ int xcd_tile(int b, int G) {
   return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
 }
 
-template <bool LORA, int RP>
+// f16 pair {s, s} of the e4m3 byte in bits 0..7 of b (exact)
+__device__ __forceinline__ uint32_t e4m3_dup_h2bits(uint32_t b) {
+  const float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(b, false);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[0]));
+}
+
+// FULL: K == 512 * SS_MAXC, so no chunk index is clamped and chunk offsets are immediates
+template <bool LORA, int RP, bool FULL>
 __global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_wide_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_wide_kernel(
   const int r16 = lane & 15, kg = lane >> 4;
   const int n0 = xcd_tile(blockIdx.x, gridDim.x) * SW_BN;
   const int kbytes = K / 2;
-  const int nc = kbytes / SS_CH;  // 1 .. SS_MAXC
+  const int nc = FULL ? SS_MAXC : kbytes / SS_CH;  // 1 .. SS_MAXC
 
   // ---- epilogue operands first: the oldest loads, complete before the first chunk is used ----
   // Every load here and below is unconditional (indices clamped), so none is moved past its use.
@@ -472,18 +479,18 @@ __global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_wide_kernel(
 
   const uint8_t* wsrc = qw + (size_t)min(n0 + (t >> 4), N - 1) * kbytes + 16 * (t & 15);
   const uint8_t* asrc = qa + (size_t)min(t >> 6, M - 1) * kbytes + 4 * (t & 63);
-  const uint8_t* ssrc = sw + (size_t)(t >> 5) * N + min(n0 + 2 * (t & 31), N - 2);
-  const uint8_t* assrc = sa + (size_t)((t & 511) >> 4) * M + min(t & 15, M - 1);
+  const uint32_t soff = (uint32_t)((t >> 5) * N + min(n0 + 2 * (t & 31), N - 2));  // within a chunk's groups
+  const uint32_t asoff = (uint32_t)(((t & 511) >> 4) * M + min(t & 15, M - 1));
   u32x4_t wr[SS_MAXC];
   uint32_t ar[SS_MAXC], sr[SS_MAXC], asr[SS_MAXC];
 // chunk j's loads (chunks past the last reload it); the scheduling barrier keeps chunks in order
 #define W4A4_SW_ISSUE(j)                                                              \
   do {                                                                                \
-    const int c_ = min((j), nc - 1);                                                  \
-    wr[(j)] = *reinterpret_cast<const u32x4_t*>(wsrc + (size_t)c_ * SS_CH);           \
-    ar[(j)] = *reinterpret_cast<const uint32_t*>(asrc + (size_t)c_ * SS_CH);          \
-    sr[(j)] = *reinterpret_cast<const uint16_t*>(ssrc + (size_t)c_ * 32 * N);         \
-    asr[(j)] = assrc[(size_t)c_ * 32 * M];                                            \
+    const int c_ = FULL ? (j) : min((j), nc - 1);                                     \
+    wr[(j)] = *reinterpret_cast<const u32x4_t*>(wsrc + c_ * SS_CH);                   \
+    ar[(j)] = *reinterpret_cast<const uint32_t*>(asrc + c_ * SS_CH);                  \
+    sr[(j)] = *reinterpret_cast<const uint16_t*>(sw + (size_t)c_ * 32 * N + soff);    \
+    asr[(j)] = (sa + (size_t)c_ * 32 * M)[asoff];                                     \
     __builtin_amdgcn_sched_barrier(0);                                                \
   } while (0)
 #pragma unroll
@@ -513,25 +520,35 @@ __global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_wide_kernel(
   for (int b = 0; b < 4; ++b) acc[b] = float4_t{0.f, 0.f, 0.f, 0.f};
   const int kb = 16 * wave + 4 * kg;   // byte of the lane's 8 codes within a chunk row
   const int g = 2 * wave + (kg >> 1);  // their 16-group within the chunk
+  // this thread's staging targets and the lane's compute operands, in slot 0
+  uint8_t* const wdst = smem + SW_W + (t >> 4) * SS_ROW + 16 * (t & 15);
+  uint8_t* const adst = smem + SW_A + (t >> 6) * SS_ROW + 4 * (t & 63);
+  uint8_t* const sdst = smem + SW_S + (t >> 5) * SW_SSTR * 4 + 8 * (t & 31);
+  uint8_t* const asdst = smem + SW_AS + (t & 511) * 4;
+  const uint8_t* const a_op = smem + SW_A + r16 * SS_ROW + kb;
+  const uint8_t* const as_op = smem + SW_AS + (g * 16 + r16) * 4;
+  const uint8_t* const w_op = smem + SW_W + r16 * SS_ROW + kb;
+  const uint8_t* const ws_op = smem + SW_S + (g * SW_SSTR + r16) * 4;
 #pragma unroll
   for (int i = 0; i < SS_MAXC; ++i) {
     if (i + SW_AHEAD < SS_MAXC) W4A4_SW_ISSUE(i + SW_AHEAD);
     // every chunk is staged, also past the last one, so the loads stay where they were issued
-    uint8_t* slot = smem + (i & 1) * SW_SLOT;
-    *reinterpret_cast<u32x4_t*>(slot + SW_W + (t >> 4) * SS_ROW + 16 * (t & 15)) = wr[i];
-    *reinterpret_cast<uint32_t*>(slot + SW_A + (t >> 6) * SS_ROW + 4 * (t & 63)) = ar[i];
-    *reinterpret_cast<u32x2_t*>(slot + SW_S + (t >> 5) * SW_SSTR * 4 + 8 * (t & 31)) =
-        u32x2_t{e4m3_to_h2bits(sr[i] & 0xFFu), e4m3_to_h2bits((sr[i] >> 8) & 0xFFu)};
-    *reinterpret_cast<uint32_t*>(slot + SW_AS + (t & 511) * 4) = e4m3_to_h2bits(asr[i]);  // halves agree
+    const int so = (i & 1) * SW_SLOT;
+    *reinterpret_cast<u32x4_t*>(wdst + so) = wr[i];
+    *reinterpret_cast<uint32_t*>(adst + so) = ar[i];
+    const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(sr[i], false);  // the two wscales, exact
+    *reinterpret_cast<u32x2_t*>(sdst + so) = u32x2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sf[0], sf[0])),
+                                                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(sf[1], sf[1]))};
+    *reinterpret_cast<uint32_t*>(asdst + so) = e4m3_dup_h2bits(asr[i]);  // both halves of the workgroup agree
     lds_barrier();  // also: every wave is done with the chunk this slot held two steps ago
-    if (i >= nc) continue;  // workgroup-uniform
-    const uint32_t a4 = *reinterpret_cast<const uint32_t*>(slot + SW_A + r16 * SS_ROW + kb);
-    const uint32_t as2 = *reinterpret_cast<const uint32_t*>(slot + SW_AS + (g * 16 + r16) * 4);
+    if (!FULL && i >= nc) continue;  // workgroup-uniform
+    const uint32_t a4 = *reinterpret_cast<const uint32_t*>(a_op + so);
+    const uint32_t as2 = *reinterpret_cast<const uint32_t*>(as_op + so);
     const half8_t av = decode8(a4, __builtin_bit_cast(half2_t, as2));
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const uint32_t w4 = *reinterpret_cast<const uint32_t*>(slot + SW_W + (16 * b + r16) * SS_ROW + kb);
-      const uint32_t ws2 = *reinterpret_cast<const uint32_t*>(slot + SW_S + (g * SW_SSTR + 16 * b + r16) * 4);
+      const uint32_t w4 = *reinterpret_cast<const uint32_t*>(w_op + so + 16 * b * SS_ROW);
+      const uint32_t ws2 = *reinterpret_cast<const uint32_t*>(ws_op + so + 16 * b * 4);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode8(w4, __builtin_bit_cast(half2_t, ws2)), av, acc[b], 0, 0,
                                                       0);
     }
@@ -608,12 +625,17 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
                     (path ? !strcmp(path, "wide") : N > 8192);
   if (wide) {
     dim3 grid((unsigned)((N + SW_BN - 1) / SW_BN)), block(64 * SW_WAVES);
-    if (!lo)
-      gemm_skinny_wide_kernel<false, 0><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
-    else if (r <= 32)
-      gemm_skinny_wide_kernel<true, 32><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
-    else
-      gemm_skinny_wide_kernel<true, 64><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+    const bool full = K == 2 * SS_CH * SS_MAXC;
+#define W4A4_SW_LAUNCH(LO, RP, FU) \
+  gemm_skinny_wide_kernel<LO, RP, FU><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp)
+    if (!lo) {
+      if (full) W4A4_SW_LAUNCH(false, 0, true); else W4A4_SW_LAUNCH(false, 0, false);
+    } else if (r <= 32) {
+      if (full) W4A4_SW_LAUNCH(true, 32, true); else W4A4_SW_LAUNCH(true, 32, false);
+    } else {
+      if (full) W4A4_SW_LAUNCH(true, 64, true); else W4A4_SW_LAUNCH(true, 64, false);
+    }
+#undef W4A4_SW_LAUNCH
     return hipGetLastError();
   }
   if (streamed) {

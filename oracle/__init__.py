@@ -26,6 +26,9 @@ Modules:
 * ``quant``    -- per-16-group FP4 quantizer, activation and weight quantizers,
                   INT4 absmax quantizer of the worked examples.
 * ``linear``   -- dequantize-then-matmul composition and the epilogue.
+* ``mx``       -- the MXFP4 variant (rotate notes, section 3.3, FP-Quant: E2M1
+                  in blocks of 32 with one E8M0 power-of-two scale, group-32
+                  rotation) with the same epilogue.
 
 Precision: every step whose result decides an integer (a code, a scale byte)
 is done in IEEE float32, the precision the GPU kernels take that decision in;
@@ -43,4 +46,4 @@ direction, scale layout, zero-scale rule, sign of zero -- are fixed readings,
 checked only for self-consistency.
 """
 
-from . import formats, hadamard, quant, linear  # noqa: F401
+from . import formats, hadamard, quant, linear, mx  # noqa: F401

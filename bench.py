@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--calib-copy", action="store_true", help="also run one 512 MiB device copy (counter calibration)")
+    ap.add_argument("--mx", action="store_true",
+                    help="the MXFP4 variant (E8M0 scale per 32, group-32 rotation) on the scaled FP4 matrix cores")
     return ap.parse_args()
 
 
@@ -53,6 +55,7 @@ def sha_of(paths):
 KERNEL_SOURCES = {
     "gemm": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "gemm_skinny": ["w4a4_bit_quantized_amd/csrc/gemm_skinny.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
+    "gemm_mx": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "quantize": ["w4a4_bit_quantized_amd/csrc/quantize.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
 }
 
@@ -74,15 +77,19 @@ def traffic_from_profile(kernel, workload):
     return 1024.0 * (ent["fetch_kib"] * cal["fetch_factor"] + ent["write_kib"] * cal["write_factor"])
 
 
-def cpu_baseline(spec_name, cpu_rows, seconds):
+def cpu_baseline(spec_name, cpu_rows, seconds, mx=False):
     """The oracle (CPU, NumPy) on a bounded row sample of the same workload."""
     import numpy as np
     from oracle import linear as olinear
+    from oracle import mx as omx
     from oracle import quant as oquant
     from w4a4_bit_quantized_amd import synth
     lay = synth.make_layer(spec_name, seed=0)
     f = synth.as_f32(lay)
-    qw, ws = oquant.quantize_weight(f["w"], f["smooth_factor"], lay["B"])  # offline, untimed
+    B = 32 if mx else lay["B"]
+    qweight_fn = omx.quantize_weight_mx if mx else oquant.quantize_weight
+    linear_fn = omx.svdq_linear_mx if mx else olinear.svdq_linear
+    qw, ws = qweight_fn(f["w"], f["smooth_factor"], B)  # offline, untimed
     rows = min(cpu_rows, lay["M"])
     layer = dict(qweight=qw, wscales=ws, **{k: f[k] for k in ("proj_down", "proj_up", "smooth_factor", "wcscales",
                                                               "wtscale")})
@@ -90,7 +97,7 @@ def cpu_baseline(spec_name, cpu_rows, seconds):
     reps, t_total = 0, 0.0
     while reps == 0 or t_total < seconds:
         t0 = time.perf_counter()
-        olinear.svdq_linear(x, layer, lay["B"])
+        linear_fn(x, layer, B)
         t_total += time.perf_counter() - t0
         reps += 1
     t = t_total / reps
@@ -140,7 +147,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    per_set = M * K * 2 + N * K // 2 + N * K // 16 + M * N * 2 + w4.svdq_linear_workspace_bytes(M, K, R)
+    if args.mx:
+        B = 32  # the MX variant rotates in blocks of 32 (its weights are quantized with the same rotation)
+    ws_bytes = w4.svdq_linear_mx_workspace_bytes if args.mx else w4.svdq_linear_workspace_bytes
+    sgroup = 32 if args.mx else 16
+    per_set = M * K * 2 + N * K // 2 + N * K // sgroup + M * N * 2 + ws_bytes(M, K, R)
     nsets = args.sets or max(1, -(-2 * MALL_BYTES // per_set))
 
     def bf(bits):
@@ -151,18 +162,20 @@ def main():
         lay = synth.make_layer(args.workload, seed=s)
         wdev = bf(lay["w"])
         lam = bf(lay["smooth_factor"])
-        qw, ws = w4.svdq_quantize_weight(wdev, lam, B)  # offline weight quantization on the GPU
+        quantize_weight = w4.svdq_quantize_weight_mx if args.mx else w4.svdq_quantize_weight
+        qw, ws = quantize_weight(wdev, lam, B)  # offline weight quantization on the GPU
         del wdev
         t = dict(x=bf(lay["x"]), qweight=qw, wscales=ws, proj_down=bf(lay["proj_down"]), proj_up=bf(lay["proj_up"]),
                  smooth_factor=lam, wcscales=bf(lay["wcscales"]), wtscale=bf(lay["wtscale"]))
         t["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        nbytes = w4.svdq_linear_workspace_bytes(M, K, R)
+        nbytes = ws_bytes(M, K, R)
         t["ws"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         # workspace views used by the two-entry-point breakdown loop (same layout as svdq_linear's)
         a256 = lambda v: (v + 255) // 256 * 256
+        srows = (M + 3) // 4 * 4 if args.mx else M
         t["qact"] = t["ws"][: M * K // 2]
-        t["ascales"] = t["ws"][a256(M * K // 2): a256(M * K // 2) + K // 16 * M]
-        off = a256(M * K // 2) + a256(K // 16 * M)
+        t["ascales"] = t["ws"][a256(M * K // 2): a256(M * K // 2) + K // sgroup * srows]
+        off = a256(M * K // 2) + a256(K // sgroup * srows)
         t["lora"] = t["ws"][off: off + M * R * 4].view(torch.float32)
         sets.append(t)
         del lay
@@ -179,8 +192,12 @@ def main():
     g_args = [(P(t["qact"]), P(t["ascales"]), P(t["lora"]), P(t["qweight"]), P(t["wscales"]), P(t["proj_up"]),
                P(t["wcscales"]), P(t["wtscale"]), M, N, K, R, P(t["y"]), sp) for t in sets]
 
+    f_linear = lib.svdq_linear_mx if args.mx else lib.svdq_linear
+    f_quant = lib.svdq_quantize_act_mx if args.mx else lib.svdq_quantize_act
+    f_gemm = lib.svdq_gemm_lowrank_mx if args.mx else lib.svdq_gemm_lowrank
+
     def step(i):
-        st = lib.svdq_linear(*lin_args[i % nsets])
+        st = f_linear(*lin_args[i % nsets])
         if st:
             raise RuntimeError(f"svdq_linear failed with status {st}")
 
@@ -199,7 +216,7 @@ def main():
                 for i in range(args.steps):
                     a = list(lin_args[i % nsets])
                     a[-1] = gsp
-                    lib.svdq_linear(*a)
+                    f_linear(*a)
         stream.wait_stream(gs)
         torch.cuda.synchronize()
 
@@ -227,10 +244,10 @@ def main():
     torch.cuda._sleep(sleep_cycles(torch, stream, 2e-3 + 40e-6 * args.steps))
     ev_q0.record(stream)
     for i in range(args.steps):
-        lib.svdq_quantize_act(*q_args[i % nsets])
+        f_quant(*q_args[i % nsets])
     ev_q1.record(stream)
     for i in range(args.steps):
-        lib.svdq_gemm_lowrank(*g_args[i % nsets])
+        f_gemm(*g_args[i % nsets])
     ev_g1.record(stream)
     torch.cuda.synchronize()
     q_us = 1e3 * ev_q0.elapsed_time(ev_q1) / args.steps
@@ -244,8 +261,8 @@ def main():
 
     flops = 2.0 * M * N * K
     value = flops / (wall_ms * 1e-3) / 1e12
-    q_bytes = M * K * 2 + K * 2 + K * R * 2 + M * K // 2 + M * K // 16 + M * R * 4
-    g_bytes = M * K // 2 + M * K // 16 + M * R * 4 + N * K // 2 + N * K // 16 + N * R * 2 + N * 2 + M * N * 2
+    q_bytes = M * K * 2 + K * 2 + K * R * 2 + M * K // 2 + M * K // sgroup + M * R * 4
+    g_bytes = M * K // 2 + M * K // sgroup + M * R * 4 + N * K // 2 + N * K // sgroup + N * R * 2 + N * 2 + M * N * 2
     kernels = {
         "quantize_act": {"avg_us": round(q_us, 3), "algorithmic_bytes": q_bytes,
                          "achieved_GBps": round(q_bytes / (q_us * 1e-6) / 1e9, 1)},
@@ -254,7 +271,11 @@ def main():
                          "achieved_GBps": round(g_bytes / (g_us * 1e-6) / 1e9, 1)},
     }
     compute_bound = M >= 256
-    if compute_bound:
+    if compute_bound and args.mx:  # the scaled FP4 instruction: priced against the FP4 peak
+        ach = flops / (g_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP4_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_FP4_MFMA_TFLOPS, 4), "kernel": "gemm_lowrank"}
+    elif compute_bound:
         ach = flops / (g_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_F16_MFMA_TFLOPS, 4), "kernel": "gemm_lowrank",
@@ -263,23 +284,24 @@ def main():
         ach = g_bytes / (g_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": "gemm_lowrank"}
-    gemm_kernel = "gemm_skinny" if M <= 32 else "gemm"
+    gemm_kernel = "gemm_mx" if args.mx else ("gemm_skinny" if M <= 32 else "gemm")
     roof["kernel"] = gemm_kernel
     tr = traffic_from_profile(gemm_kernel, args.workload)
     roof["traffic"] = None if tr is None else round(tr)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.workload, args.cpu_rows, args.cpu_seconds)
+        cpu = cpu_baseline(args.workload, args.cpu_rows, args.cpu_seconds, args.mx)
 
     line = {
         "metric": "W4A4 linear effective TFLOP/s (2MNK) and % of FP4-MFMA/HBM roofline",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall_ms, 5), "gpu_ms_per_step": round(gpu_ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "storage": "fp4 e2m1 + e4m3 per 16 (nvfp4)",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4" if args.mx else "f16",
+        "storage": "fp4 e2m1 + e8m0 per 32 (mxfp4)" if args.mx else "fp4 e2m1 + e4m3 per 16 (nvfp4)",
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "K": K, "N": N, "R": R, "hadamard_block": B,
-                   "input_sets": nsets, "graph": bool(args.graph)},
+        "config": {"workload": args.workload + ("_mx" if args.mx else ""), "M": M, "K": K, "N": N, "R": R,
+                   "hadamard_block": B, "input_sets": nsets, "graph": bool(args.graph)},
         "frac_of_fp4_peak": round(value / PEAK_FP4_MFMA_TFLOPS, 4),
         "kernels": kernels, "roofline": roof, "cpu_baseline": cpu,
     }

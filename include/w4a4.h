@@ -144,6 +144,53 @@ w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales,
                         int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+
+/*
+ * MXFP4 variant of the layer (rotate notes, section 3.3, FP-Quant:
+ * hadamard_group_size 32, forward_dtype "mxfp4", forward_method "abs_max";
+ * fused_quantize_mx then matmul_mxf4_bf16).  Smoothing, the optional rotation
+ * and the low-rank branch are those of the entry points above; the
+ * quantization works on blocks of 32 consecutive K-columns with one E8M0
+ * (power-of-two) scale per block instead of 16-groups with e4m3 scales:
+ *   e     = the least integer with 2^e >= f32(amax|v| / 6), clamped to [-127, 127]
+ *   scale byte = e + 127  (E8M0: value 2^(byte - 127))
+ *   code  = e2m1(v * 2^-e)   (round-to-nearest-even, saturating at 6, sign kept)
+ * and the GEMM multiplies E2M1 codes scaled by 2^(byte - 127) per row and block
+ * (matrix-core instruction with per-block power-of-two scales), fp32
+ * accumulation, the same epilogue.  Inputs must be finite.
+ *
+ * svdq_quantize_act_mx: as svdq_quantize_act with K % 32 == 0 and
+ *   hadamard_block 0 or 32;
+ *   ascales  u8 [K/32, Mp] out   Mp = 4 * ceil(M / 4); columns M .. Mp-1 are written 0
+ * svdq_quantize_weight_mx: as svdq_quantize_weight with K % 32 == 0 and
+ *   hadamard_block 0 or 32;  wscales u8 [K/32, N] out
+ * svdq_gemm_lowrank_mx: as svdq_gemm_lowrank with K % 128 == 0, N % 4 == 0;
+ *   ascales u8 [K/32, Mp] and wscales u8 [K/32, N], both 4-byte aligned
+ * svdq_linear_mx: svdq_quantize_act_mx into the workspace (at least
+ *   svdq_linear_mx_workspace_bytes(M, K, R) bytes, 256-byte aligned), then
+ *   svdq_gemm_lowrank_mx.
+ * Other sizes return W4A4_ERR_SHAPE (K, N) or W4A4_ERR_UNSUPPORTED (hadamard_block).
+ */
+w4a4_status svdq_quantize_act_mx(const void* x, const void* smooth_factor, const void* proj_down,
+                                 int64_t M, int64_t K, int64_t R, int32_t hadamard_block,
+                                 void* qact, void* ascales, float* lora_act, void* stream);
+
+w4a4_status svdq_quantize_weight_mx(const void* w, const void* smooth_factor, int64_t N, int64_t K,
+                                    int32_t hadamard_block, void* qweight, void* wscales, void* stream);
+
+w4a4_status svdq_gemm_lowrank_mx(const void* qact, const void* ascales, const float* lora_act,
+                                 const void* qweight, const void* wscales, const void* proj_up,
+                                 const void* wcscales, const void* wtscale,
+                                 int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream);
+
+size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int64_t R);
+
+w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                           const void* proj_up, const void* smooth_factor, const void* wcscales,
+                           const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R,
+                           int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

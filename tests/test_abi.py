@@ -126,3 +126,25 @@ def test_binding_signatures_match_header(lib):
         fn = getattr(lib, name)
         assert fn.argtypes == args and fn.restype == res
     assert ctypes.sizeof(ctypes.c_size_t) == 8
+
+
+# ---- MXFP4 entry points -----------------------------------------------------------------------
+
+def test_mx_validation(lib):
+    qa = lambda **k: lib.svdq_quantize_act_mx(k.get("x", P), P, P, k.get("M", 16), k.get("K", 128), k.get("R", 32),
+                                               k.get("hb", 32), P, P, P, None)
+    assert qa(K=48) == ERR_SHAPE           # K % 32
+    assert qa(hb=16) == ERR_UNSUPPORTED    # rotation in blocks of 32 or none
+    assert qa(hb=128) == ERR_UNSUPPORTED
+    assert qa(x=None) == ERR_NULL
+    assert qa(M=0, x=None) == OK
+    qw = lambda **k: lib.svdq_quantize_weight_mx(P, P, k.get("N", 8), k.get("K", 64), k.get("hb", 0), P, P, None)
+    assert qw(K=80) == ERR_SHAPE and qw(hb=64) == ERR_UNSUPPORTED and qw(N=0) == OK
+    g = lambda **k: lib.svdq_gemm_lowrank_mx(P, k.get("sa", P), P, P, k.get("sw", P), P, P, P, k.get("M", 16),
+                                              k.get("N", 64), k.get("K", 256), k.get("R", 32), P, None)
+    assert g(K=96) == ERR_SHAPE            # whole 128-column K-steps
+    assert g(N=66) == ERR_SHAPE            # N % 4
+    assert g(sa=P + 2) == ERR_ALIGN and g(sw=P + 1) == ERR_ALIGN
+    assert g(M=0) == OK
+    assert lib.svdq_linear_mx_workspace_bytes(6, 256, 32) == 768 + 256 + 768  # codes, scales (8 x 8 rows), lora
+    assert lib.svdq_linear_mx_workspace_bytes(6, 48, 32) == 0

@@ -1,0 +1,158 @@
+"""GPU parity of the MXFP4 variant (rotate notes, section 3.3: FP-Quant mxfp4 with a group-32
+rotation) against the CPU oracle ``oracle/mx.py`` (needs an MI355X).
+
+Bars as for the nvfp4 path: codes and E8M0 scale bytes bit-exact (including the zero padding
+of the activation scale rows), lora_act within the float32 accumulation bound of the hi/lo
+bf16 split, bf16 outputs within relative Frobenius 5e-3 and max |diff| 2e-2 max|y_ref| plus
+a per-element float32 accumulation bound.  Every call goes through the C ABI.
+"""
+
+import numpy as np
+import pytest
+
+import helpers as H
+from oracle import mx as omx
+from oracle import quant as oquant
+from w4a4_bit_quantized_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w4():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import w4a4_bit_quantized_amd as w
+    w.load_library()
+    return w
+
+
+def _lay(M, K, N, R, B, seed):
+    return synth.make_layer("tiny", seed=seed, M=M, K=K, N=N, R=R, B=B, wcs="uniform")
+
+
+def _mx_weights(lay):
+    f = synth.as_f32(lay)
+    return omx.quantize_weight_mx(f["w"], f["smooth_factor"], lay["B"])
+
+
+def _lora_bound(xs, pd, K):
+    b = np.abs(xs.astype(np.float64)) @ np.abs(pd.astype(np.float64))
+    return (2.0 ** -18 + (2 * K // 32 + 64) * 2.0 ** -24) * b + 1e-30
+
+
+@pytest.mark.parametrize("M,K,R,B", [(16, 128, 32, 32), (37, 256, 8, 0), (3, 64, 0, 32), (130, 512, 64, 32),
+                                     (64, 1024, 16, 0), (5, 96, 32, 32)])
+def test_quantize_act_mx_parity(w4, M, K, R, B):
+    import torch
+    lay = _lay(M, K, 64, R, B, seed=M + K)
+    f = synth.as_f32(lay)
+    qa, sa, lo = w4.svdq_quantize_act_mx(H.to_dev_bf16(lay["x"]), H.to_dev_bf16(lay["smooth_factor"]),
+                                         H.to_dev_bf16(lay["proj_down"]), B)
+    torch.cuda.synchronize()
+    q_ref, s_ref, l_ref = omx.quantize_act_mx(f["x"], f["smooth_factor"], f["proj_down"], B)
+    assert sa.shape == s_ref.shape
+    bad = np.argwhere(qa.cpu().numpy() != q_ref)
+    assert bad.size == 0, f"{len(bad)} code bytes differ, first at {bad[:3].tolist()}"
+    bad = np.argwhere(sa.cpu().numpy() != s_ref)
+    assert bad.size == 0, f"{len(bad)} scale bytes differ, first at {bad[:3].tolist()}"
+    if R:
+        xs = oquant.smooth(f["x"], f["smooth_factor"])
+        err = np.abs(lo.cpu().numpy().astype(np.float64) - l_ref)
+        assert np.all(err <= _lora_bound(xs, f["proj_down"], K))
+
+
+@pytest.mark.parametrize("N,K,B", [(8, 64, 0), (33, 96, 32), (256, 1024, 32), (130, 512, 0)])
+def test_quantize_weight_mx_parity(w4, N, K, B):
+    import torch
+    lay = _lay(4, K, N, 8, B, seed=N + K)
+    qw, sw = w4.svdq_quantize_weight_mx(H.to_dev_bf16(lay["w"]), H.to_dev_bf16(lay["smooth_factor"]), B)
+    torch.cuda.synchronize()
+    q_ref, s_ref = _mx_weights(lay)
+    assert np.array_equal(qw.cpu().numpy(), q_ref)
+    assert np.array_equal(sw.cpu().numpy(), s_ref)
+
+
+def _accumulation_bound(qa, sa, lo, qw, sw, pu, wcs, wts, M, N, n_adds):
+    a = np.abs(omx.dequant_mx(qa, sa, M))
+    w = np.abs(omx.dequant_mx(qw, sw, N))
+    c = np.abs(np.asarray(wcs, np.float64) * float(np.asarray(wts, np.float64).reshape(-1)[0]))
+    b = (a @ w.T) * c[None, :]
+    if np.asarray(pu).shape[1]:
+        b = b + np.abs(np.asarray(lo, np.float64)) @ np.abs(np.asarray(pu, np.float64)).T
+    return n_adds * 2.0 ** -24 * b
+
+
+def _check_gemm_mx(w4, lay):
+    import torch
+    f = synth.as_f32(lay)
+    M, N, K = lay["M"], lay["N"], lay["K"]
+    qw, sw = _mx_weights(lay)
+    qa, sa, lo = omx.quantize_act_mx(f["x"], f["smooth_factor"], f["proj_down"], lay["B"])
+    lo32 = lo.astype(np.float32)
+    y = w4.svdq_gemm_lowrank_mx(H.to_dev_u8(qa), H.to_dev_u8(sa), torch.from_numpy(lo32).cuda(), H.to_dev_u8(qw),
+                                H.to_dev_u8(sw), H.to_dev_bf16(lay["proj_up"]), H.to_dev_bf16(lay["wcscales"]),
+                                H.to_dev_bf16(lay["wtscale"]))
+    torch.cuda.synchronize()
+    _, y_ref = omx.gemm_lowrank_mx(qa, sa, lo32, qw, sw, f["proj_up"], f["wcscales"], f["wtscale"])
+    y_gpu = H.from_dev_bf16_f64(y)
+    H.assert_gates(y_gpu, y_ref, "gemm_mx")
+    bound = _accumulation_bound(qa, sa, lo32, qw, sw, f["proj_up"], f["wcscales"], f["wtscale"], M, N,
+                                n_adds=K // 32 + 4 * lay["R"] + 64)
+    err = np.abs(y_gpu - y_ref)
+    lim = 2.0 ** -8 * np.abs(y_ref) + bound + 1e-30
+    assert np.all(err <= lim), f"per-element bound broken: worst excess {np.max(err - lim):.3e}"
+
+
+@pytest.mark.parametrize("M,N,K,R", [(64, 256, 256, 32), (130, 200, 384, 8), (37, 68, 128, 0), (3, 40, 256, 64),
+                                     (300, 520, 640, 32), (512, 512, 1024, 16)])
+def test_gemm_lowrank_mx_parity(w4, M, N, K, R):
+    _check_gemm_mx(w4, _lay(M, K, N, R, 32, seed=M * 7 + N))
+
+
+@pytest.mark.parametrize("tile", ["2x4x4x2", "2x2x2x2"])
+def test_gemm_mx_each_tile(w4, tile, monkeypatch):
+    monkeypatch.setenv("W4A4_GEMM_TILE", tile)
+    _check_gemm_mx(w4, _lay(300, 640, 520, 32, 0, seed=41))
+
+
+@pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 32), (37, 68, 384, 16, 0), (16, 200, 2048, 32, 32),
+                                       (5, 132, 512, 8, 32)])
+def test_linear_mx_parity(w4, M, N, K, R, B):
+    import torch
+    lay = _lay(M, K, N, R, B, seed=3 + M)
+    qw, sw = _mx_weights(lay)
+    y = w4.svdq_linear_mx(H.to_dev_bf16(lay["x"]), H.device_layer(lay, qw, sw), hadamard_block=B)
+    torch.cuda.synchronize()
+    f = synth.as_f32(lay)
+    layer = dict(qweight=qw, wscales=sw, proj_down=f["proj_down"], proj_up=f["proj_up"],
+                 smooth_factor=f["smooth_factor"], wcscales=f["wcscales"], wtscale=f["wtscale"])
+    _, y_ref, _ = omx.svdq_linear_mx(f["x"], layer, B)
+    H.assert_gates(H.from_dev_bf16_f64(y), y_ref, "svdq_linear_mx")
+
+
+def test_linear_mx_full_size_dit_mlp_up(w4):
+    """The DiT MLP up-projection shape (M=4096, K=3072, N=12288, R=32) through the MX layer with a
+    group-32 rotation, checked on sampled rows and columns."""
+    import torch
+    lay = synth.make_layer("dit_mlp_up", seed=0)
+    M, N, K = lay["M"], lay["N"], lay["K"]
+    rng = np.random.default_rng(321)
+    rows = np.sort(rng.choice(M, 32, replace=False))
+    cols = np.sort(rng.choice(N, 192, replace=False))
+    qw_d, sw_d = w4.svdq_quantize_weight_mx(H.to_dev_bf16(lay["w"]), H.to_dev_bf16(lay["smooth_factor"]), 32)
+    f = synth.as_f32(lay)
+    qw_ref, sw_ref = omx.quantize_weight_mx(f["w"][cols], f["smooth_factor"], 32)
+    torch.cuda.synchronize()
+    assert np.array_equal(qw_d.cpu().numpy()[cols], qw_ref)
+    assert np.array_equal(sw_d.cpu().numpy()[:, cols], sw_ref)
+    layer = H.device_layer(lay, np.zeros((1, 1), np.uint8), np.zeros((1, 1), np.uint8))
+    layer["qweight"], layer["wscales"] = qw_d, sw_d
+    y = w4.svdq_linear_mx(H.to_dev_bf16(lay["x"]), layer, hadamard_block=32)
+    torch.cuda.synchronize()
+    y_gpu = H.from_dev_bf16_f64(y)[np.ix_(rows, cols)]
+    sub = dict(qweight=qw_ref, wscales=sw_ref, proj_down=f["proj_down"], proj_up=f["proj_up"][cols],
+               smooth_factor=f["smooth_factor"], wcscales=f["wcscales"][cols], wtscale=f["wtscale"])
+    _, y_ref, _ = omx.svdq_linear_mx(f["x"][rows], sub, 32)
+    rel, mx = H.assert_gates(y_gpu, y_ref, "dit_mlp_up mx")
+    print(f"\ndit_mlp_up mx: parity rel_fro={rel:.2e} max={mx:.2e}")

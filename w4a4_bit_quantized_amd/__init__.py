@@ -19,4 +19,9 @@ from .binding import (  # noqa: F401
     svdq_linear_workspace_bytes,
     svdq_quantize_act,
     svdq_quantize_weight,
+    svdq_gemm_lowrank_mx,
+    svdq_linear_mx,
+    svdq_linear_mx_workspace_bytes,
+    svdq_quantize_act_mx,
+    svdq_quantize_weight_mx,
 )

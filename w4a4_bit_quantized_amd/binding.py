@@ -30,6 +30,14 @@ SIGNATURES = {
     "svdq_linear_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "svdq_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                    _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "svdq_quantize_act_mx": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p,
+                                            _c_p]),
+    "svdq_quantize_weight_mx": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+    "svdq_gemm_lowrank_mx": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                            _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "svdq_linear_mx_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
+    "svdq_linear_mx": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                      _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t, _c_p]),
 }
 
 
@@ -206,4 +214,104 @@ def svdq_linear(x, layer, hadamard_block=0, workspace=None, out=None):
                          M, N, K, R, int(hadamard_block), _ptr(y), _ptr(workspace),
                          workspace.numel(), _stream(dev))
     _check(st, "svdq_linear")
+    return y.reshape(*lead, N)
+
+
+# ---- MXFP4 variant (E2M1 in blocks of 32 with one E8M0 scale per block) ---------------------
+
+def mx_scale_rows(M):
+    """Row stride of the MX activation scale tensor: M rounded up to a multiple of 4."""
+    return (int(M) + 3) // 4 * 4
+
+
+def svdq_linear_mx_workspace_bytes(M, K, R):
+    return int(load_library().svdq_linear_mx_workspace_bytes(int(M), int(K), int(R)))
+
+
+def svdq_quantize_act_mx(x, smooth_factor, proj_down, hadamard_block=32):
+    """x (M, K) bf16 -> (qact (M, K/2) u8, ascales (K/32, Mp) u8 E8M0, lora_act (M, R) f32)."""
+    torch = _torch()
+    lib = load_library()
+    x = _dev(x, "x", (torch.bfloat16,))
+    dev = x.device
+    M, K = x.shape
+    _dev(smooth_factor, "smooth_factor", (torch.bfloat16,), dev)
+    _dev(proj_down, "proj_down", (torch.bfloat16,), dev)
+    R = proj_down.shape[1]
+    qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    ascales = torch.empty((K // 32, mx_scale_rows(M)), dtype=torch.uint8, device=dev)
+    lora = torch.empty((M, R), dtype=torch.float32, device=dev)
+    st = lib.svdq_quantize_act_mx(_ptr(x), _ptr(smooth_factor), _ptr(proj_down), M, K, R, int(hadamard_block),
+                                  _ptr(qact), _ptr(ascales), _ptr(lora), _stream(dev))
+    _check(st, "svdq_quantize_act_mx")
+    return qact, ascales, lora
+
+
+def svdq_quantize_weight_mx(w, smooth_factor, hadamard_block=32):
+    """w (N, K) bf16 -> (qweight (N, K/2) u8, wscales (K/32, N) u8 E8M0)."""
+    torch = _torch()
+    lib = load_library()
+    w = _dev(w, "w", (torch.bfloat16,))
+    dev = w.device
+    N, K = w.shape
+    _dev(smooth_factor, "smooth_factor", (torch.bfloat16,), dev)
+    qweight = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    wscales = torch.empty((K // 32, N), dtype=torch.uint8, device=dev)
+    st = lib.svdq_quantize_weight_mx(_ptr(w), _ptr(smooth_factor), N, K, int(hadamard_block),
+                                     _ptr(qweight), _ptr(wscales), _stream(dev))
+    _check(st, "svdq_quantize_weight_mx")
+    return qweight, wscales
+
+
+def svdq_gemm_lowrank_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, out=None):
+    """MXFP4 GEMM + epilogue -> y (M, N) bf16."""
+    torch = _torch()
+    lib = load_library()
+    qact = _dev(qact, "qact", _bytes_dtypes())
+    dev = qact.device
+    _dev(ascales, "ascales", (torch.uint8,), dev)
+    _dev(lora_act, "lora_act", (torch.float32,), dev)
+    _dev(qweight, "qweight", _bytes_dtypes(), dev)
+    _dev(wscales, "wscales", (torch.uint8,), dev)
+    _dev(proj_up, "proj_up", (torch.bfloat16,), dev)
+    _dev(wcscales, "wcscales", (torch.bfloat16,), dev)
+    _dev(wtscale, "wtscale", (torch.bfloat16,), dev)
+    M, K = qact.shape[0], qact.shape[1] * 2
+    N = qweight.shape[0]
+    R = proj_up.shape[1]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _dev(y, "y", (torch.bfloat16,), dev)
+    st = lib.svdq_gemm_lowrank_mx(_ptr(qact), _ptr(ascales), _ptr(lora_act), _ptr(qweight), _ptr(wscales),
+                                  _ptr(proj_up), _ptr(wcscales), _ptr(wtscale), M, N, K, R, _ptr(y), _stream(dev))
+    _check(st, "svdq_gemm_lowrank_mx")
+    return y
+
+
+def svdq_linear_mx(x, layer, hadamard_block=32, workspace=None, out=None):
+    """The whole MXFP4 layer (``layer`` as for ``svdq_linear``, with MX qweight / wscales)."""
+    torch = _torch()
+    lib = load_library()
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    _dev(x2, "x", (torch.bfloat16,))
+    dev = x2.device
+    M, K = x2.shape
+    t = {k: layer[k] for k in LAYER_KEYS}
+    _dev(t["qweight"], "qweight", _bytes_dtypes(), dev)
+    _dev(t["wscales"], "wscales", (torch.uint8,), dev)
+    for k in ("proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale"):
+        _dev(t[k], k, (torch.bfloat16,), dev)
+    N = t["qweight"].shape[0]
+    R = t["proj_up"].shape[1]
+    need = int(lib.svdq_linear_mx_workspace_bytes(M, K, R))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", (torch.uint8,), dev)
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _dev(y, "y", (torch.bfloat16,), dev)
+    st = lib.svdq_linear_mx(_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]),
+                            _ptr(t["proj_up"]), _ptr(t["smooth_factor"]), _ptr(t["wcscales"]), _ptr(t["wtscale"]),
+                            M, N, K, R, int(hadamard_block), _ptr(y), _ptr(workspace),
+                            workspace.numel(), _stream(dev))
+    _check(st, "svdq_linear_mx")
     return y.reshape(*lead, N)

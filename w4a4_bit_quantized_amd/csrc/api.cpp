@@ -148,3 +148,112 @@ w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales,
 }
 
 }  // extern "C"
+
+// ---- MXFP4 variant -----------------------------------------------------------------------
+
+namespace {
+
+int64_t mx_rows(int64_t M) { return (M + 3) / 4 * 4; }
+
+w4a4_status check_mx(int64_t K, int64_t R, int32_t hb, bool gemm) {
+  if (hb != 0 && hb != 32) return W4A4_ERR_UNSUPPORTED;
+  w4a4_status st = check_k_rank_block(K, R, hb);
+  if (st != W4A4_OK) return st;
+  if (K % (gemm ? 128 : 32) != 0) return W4A4_ERR_SHAPE;
+  return W4A4_OK;
+}
+
+w4a4_status validate_gemm_mx(const void* qact, const void* ascales, const float* lora, const void* qweight,
+                             const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
+                             int64_t M, int64_t N, int64_t K, int64_t R, const void* y) {
+  w4a4_status st = check_mx(K, R, 0, true);
+  if (st != W4A4_OK) return st;
+  if (N % 4 != 0) return W4A4_ERR_SHAPE;
+  st = validate_gemm(qact, ascales, lora, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if (!aligned(ascales, 4) || !aligned(wscales, 4)) return W4A4_ERR_ALIGN;
+  return W4A4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a4_status svdq_quantize_act_mx(const void* x, const void* smooth_factor, const void* proj_down, int64_t M,
+                                 int64_t K, int64_t R, int32_t hadamard_block, void* qact, void* ascales,
+                                 float* lora_act, void* stream) {
+  w4a4_status st = check_mx(K, R, hadamard_block, false);
+  if (st != W4A4_OK) return st;
+  st = validate_quantize_act(x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales, lora_act);
+  if (st != W4A4_OK || M == 0) return st;
+  (void)hipGetLastError();
+  return from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, 1, qact, ascales,
+                                        lora_act, static_cast<hipStream_t>(stream), true, mx_rows(M)));
+}
+
+w4a4_status svdq_quantize_weight_mx(const void* w, const void* smooth_factor, int64_t N, int64_t K,
+                                    int32_t hadamard_block, void* qweight, void* wscales, void* stream) {
+  w4a4_status st = check_mx(K, 0, hadamard_block, false);
+  if (st != W4A4_OK) return st;
+  if (N < 0 || N > kMaxDim) return W4A4_ERR_SHAPE;
+  if (N == 0) return W4A4_OK;
+  if (!w || !smooth_factor || !qweight || !wscales) return W4A4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(smooth_factor, 16) || !aligned(qweight, 4)) return W4A4_ERR_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(w4a4::launch_quantize(false, w, smooth_factor, nullptr, N, K, 0, hadamard_block, 1, qweight,
+                                        wscales, nullptr, static_cast<hipStream_t>(stream), true, N));
+}
+
+w4a4_status svdq_gemm_lowrank_mx(const void* qact, const void* ascales, const float* lora_act, const void* qweight,
+                                 const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
+                                 int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream) {
+  w4a4_status st =
+      validate_gemm_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  (void)hipGetLastError();
+  return from_hip(w4a4::launch_gemm_mx(qact, ascales, lora_act, 1, qweight, wscales, proj_up, wcscales, wtscale, M,
+                                       N, K, R, mx_rows(M), y, static_cast<hipStream_t>(stream)));
+}
+
+size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+  if (M < 0 || M > kMaxDim || check_mx(K, R, 0, false) != W4A4_OK) return 0;
+  const size_t m = (size_t)M, k = (size_t)K, r = (size_t)R;
+  const size_t parts = (size_t)w4a4::quantize_parts(M, K);
+  return align256(m * k / 2) + align256(k / 32 * (size_t)mx_rows(M)) + align256(parts * m * r * sizeof(float));
+}
+
+w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                           const void* proj_up, const void* smooth_factor, const void* wcscales, const void* wtscale,
+                           int64_t M, int64_t N, int64_t K, int64_t R, int32_t hadamard_block, void* y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  w4a4_status st = check_mx(K, R, hadamard_block, true);
+  if (st != W4A4_OK) return st;
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || N % 4 != 0) return W4A4_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!x || !qweight || !wscales || !smooth_factor || !wcscales || !wtscale || !y) return W4A4_ERR_NULL;
+  if (R > 0 && (!proj_down || !proj_up)) return W4A4_ERR_NULL;
+  if (!workspace) return W4A4_ERR_NULL;
+  const size_t need = svdq_linear_mx_workspace_bytes(M, K, R);
+  if (workspace_bytes < need) return W4A4_ERR_SHAPE;
+  if (!aligned(workspace, 256)) return W4A4_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void* qact = ws;
+  void* ascales = ws + align256((size_t)M * K / 2);
+  float* lora = R > 0 ? reinterpret_cast<float*>(ws + align256((size_t)M * K / 2) +
+                                                 align256((size_t)K / 32 * (size_t)mx_rows(M)))
+                      : nullptr;
+  st = validate_quantize_act(x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales, lora);
+  if (st != W4A4_OK) return st;
+  st = validate_gemm_mx(qact, ascales, lora, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
+  if (st != W4A4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int parts = w4a4::quantize_parts(M, K);
+  st = from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, parts, qact, ascales,
+                                      lora, s, true, mx_rows(M)));
+  if (st != W4A4_OK) return st;
+  return from_hip(w4a4::launch_gemm_mx(qact, ascales, lora, parts, qweight, wscales, proj_up, wcscales, wtscale, M, N,
+                                       K, R, mx_rows(M), y, s));
+}
+
+}  // extern "C"

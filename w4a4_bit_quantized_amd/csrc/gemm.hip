@@ -635,6 +635,164 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
   epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
 }
 
+// ---- MXFP4 variant (rotate notes, section 3.3: FP-Quant mxfp4, matmul_mxf4_bf16) ----------
+// Codes as above; one E8M0 scale per 32 K-columns, (K/32, rows) tensors whose dwords are 4
+// consecutive rows of one block.  The product runs on the scaled FP4 matrix instruction
+// v_mfma_scale_f32_32x32x64_f8f6f4, which takes the packed E2M1 codes directly and applies a
+// power-of-two scale per row and 32-column block: no decode.  Lane l of an operand supplies row
+// l % 32, K-columns 32 (l / 32) .. +32 of the instruction's 64 (16 bytes in the first four
+// registers) and, in byte `opsel` of its scale register, the E8M0 byte of that row and block.
+// A K-step of 128 columns is two instructions; lane half h reads code chunks h and 2 + h of
+// its row and the scales of blocks h and 2 + h.  The accumulator layout equals the f16
+// kernel's, so the epilogue is shared.
+template <class T>
+struct DmaTileMx {
+  static constexpr int WAVES = T::WM * T::WN;
+  static constexpr int ROUND_ROWS = 16 * WAVES;
+  static constexpr int ROUNDS = (T::ROWS + ROUND_ROWS - 1) / ROUND_ROWS;
+  static constexpr int SDW = T::ROWS;             // scale dwords per K-step: ROWS/4 quads x 4 blocks
+  static constexpr int SROUNDS = (SDW + 64 * WAVES - 1) / (64 * WAVES);
+  static constexpr int SCALE_OFF = ROUNDS * ROUND_ROWS * 64;
+  static constexpr int STAGE = SCALE_OFF + SROUNDS * WAVES * 256;
+  static constexpr int LOADS = ROUNDS + SROUNDS;
+  static constexpr int LDS_BYTES = 3 * STAGE > T::EPI_BYTES ? 3 * STAGE : T::EPI_BYTES;
+  static_assert(T::BM % 16 == 0 && T::ROWS % 16 == 0, "whole 16-row blocks");
+};
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// `ms` is the row stride of the activation scale tensor (M rounded up to 4).
+template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
+    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R, int ms,
+    uint16_t* __restrict__ y) {
+  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
+  using D = DmaTileMx<T>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[D::LDS_BYTES];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int tiles_n = (N + T::BN - 1) / T::BN;
+  const int n0 = (int)(blockIdx.x % tiles_n) * T::BN;
+  const int m0 = (int)(blockIdx.x / tiles_n) * T::BM;
+  const uint32_t kbytes = (uint32_t)K / 2;
+  const int nkt = K / BK;
+  const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);
+  const int srows_a = min(T::BM, ms - m0);  // scale rows: whole quads (ms % 4 == 0, N % 4 == 0)
+
+  const uint8_t* c_base[D::ROUNDS];
+  uint32_t c_off[D::ROUNDS];
+#pragma unroll
+  for (int r = 0; r < D::ROUNDS; ++r) {
+    const int row = r * D::ROUND_ROWS + wave * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const bool is_a = row < T::BM;
+    const int src = is_a ? min(row, rows_a - 1) : min(row - T::BM, rows_b - 1);
+    c_base[r] = is_a ? qa + (size_t)m0 * kbytes : qw + (size_t)n0 * kbytes;
+    c_off[r] = (uint32_t)src * kbytes + 16u * (uint32_t)c;
+  }
+  // scale dword of each round: LDS dword index d -> quad d / 4 (tile rows 4 quad ..), block d % 4
+  const uint8_t* s_base[D::SROUNDS];
+  uint32_t s_off[D::SROUNDS], s_stride[D::SROUNDS];
+#pragma unroll
+  for (int r = 0; r < D::SROUNDS; ++r) {
+    const int d = min((r * D::WAVES + wave) * 64 + lane, D::SDW - 1);
+    const int quad = d >> 2, g = d & 3;
+    const bool is_a = 4 * quad < T::BM;
+    const int row = is_a ? min(4 * quad, srows_a - 4) : min(4 * quad - T::BM, rows_b - 4);
+    s_base[r] = is_a ? sa + m0 : sw + n0;
+    s_stride[r] = is_a ? (uint32_t)ms : (uint32_t)N;
+    s_off[r] = (uint32_t)g * s_stride[r] + (uint32_t)row;
+  }
+
+  // K-step kt covers 4 scale blocks: block rows 4 kt .. 4 kt + 3 of the scale tensors
+  dma_issue<D>(lds, wave, 0u, (size_t)0, c_base, c_off, s_base, s_off, s_stride);
+  dma_issue<D>(lds + D::STAGE, wave, (uint32_t)(nkt > 1 ? 1 : 0) * (BK / 2), (size_t)(nkt > 1 ? 1 : 0) * (BK / 32),
+               c_base, c_off, s_base, s_off, s_stride);
+  vm_wait_barrier<0>();
+
+  float16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // byte of the lane's row in a scale dword: result byte 0 from the block-h dword, byte 1 from
+  // the block-(2 + h) dword
+  const uint32_t psel = (uint32_t)(l32 & 3) | ((uint32_t)(4 + (l32 & 3)) << 8) | 0x0C0C0000u;
+  int slot = 0;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int slot2 = slot == 0 ? 2 : slot - 1;
+    const int kn = min(kt + 2, nkt - 1);
+    dma_issue<D>(lds + slot2 * D::STAGE, wave, (uint32_t)kn * (BK / 2), (size_t)kn * (BK / 32), c_base, c_off, s_base,
+                 s_off, s_stride);
+    const uint8_t* cur = lds + slot * D::STAGE;
+    uint32_t sA[FM], sB[FN];
+    i32x8_t cA[2][FM], cB[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * FM * 32 + i * 32 + l32;
+      const int sw4 = (row >> 1) & 3;
+      const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+      sA[i] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const i32x4_t c = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
+        cA[s2][i] = __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1);  // upper half unread for FP4
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = T::BM + wn * FN * 32 + j * 32 + l32;
+      const int sw4 = (row >> 1) & 3;
+      const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+      sB[j] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const i32x4_t c = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
+        cB[s2][j] = __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1);
+      }
+    }
+    // weights first (output columns n), activations second (output rows m), as in the f16 kernel
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cB[0][j], cA[0][i], acc[i][j], 4, 4, 0, sB[j], 0,
+                                                                    sA[i]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cB[1][j], cA[1][i], acc[i][j], 4, 4, 1, sB[j], 1,
+                                                                    sA[i]);
+      }
+    vm_wait_barrier<D::LOADS>();
+    slot = slot == 2 ? 0 : slot + 1;
+  }
+  vm_wait_barrier<0>();
+
+  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
+}
+
+template <int WAVES_M, int WAVES_N, int FM, int FN>
+hipError_t launch_mx_tile(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
+                          const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
+                          const uint16_t* wts, int M, int N, int K, int R, int ms, uint16_t* y) {
+  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
+  dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
+  dim3 block(T::THREADS);
+  if (rb > 0)
+    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
+  else
+    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
+  return hipGetLastError();
+}
+
 template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16>
 hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                      const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
@@ -751,6 +909,28 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
       return launch_tile<4, 2, 2, 3>(dma, rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
   }
 #undef W4A4_TILE_CASE
+}
+
+hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lora, int lora_parts,
+                          const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
+                          const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, int64_t ms, void* y,
+                          hipStream_t stream) {
+  const int rb = (int)((R + 15) / 16);
+  auto qa = static_cast<const uint8_t*>(qact);
+  auto sa = static_cast<const uint8_t*>(ascales);
+  auto qw = static_cast<const uint8_t*>(qweight);
+  auto sw = static_cast<const uint8_t*>(wscales);
+  auto pu = static_cast<const uint16_t*>(proj_up);
+  auto wc = static_cast<const uint16_t*>(wcscales);
+  auto wt = static_cast<const uint16_t*>(wtscale);
+  auto yp = static_cast<uint16_t*>(y);
+  const int m = (int)M, n = (int)N, k = (int)K, r = (int)R, s = (int)ms;
+  // 8-wave 256 x 256 tiles when they fill the chip, else 4-wave 128 x 128; W4A4_GEMM_TILE=2x4x4x2 or
+  // 2x2x2x2 forces one
+  const char* forced = getenv("W4A4_GEMM_TILE");
+  const bool big = forced ? !strcmp(forced, "2x4x4x2") : tile_score(M, N, 256, 256) >= tile_score(M, N, 128, 128);
+  if (big) return launch_mx_tile<2, 4, 4, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
+  return launch_mx_tile<2, 2, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
 }
 
 }  // namespace w4a4

@@ -11,9 +11,11 @@ namespace w4a4 {
 // or weight (act = false: multiply by smooth_factor) quantizer over `rows` x K.
 // With parts > 1, K is split across workgroups and lora receives `parts`
 // partial sums, each [rows, R], laid out one after another.
+// With mx, the scales are MXFP4 E8M0 bytes per 32 columns in rows of scale_stride bytes
+// (scale_stride >= rows; entries rows .. scale_stride - 1 receive 0) and hadamard_block is 0 or 32.
 hipError_t launch_quantize(bool act, const void* x, const void* lam, const void* pd, int64_t rows, int64_t K,
                            int64_t R, int hadamard_block, int parts, void* q, void* scales, float* lora,
-                           hipStream_t stream);
+                           hipStream_t stream, bool mx = false, int64_t scale_stride = 0);
 
 // Batches up to this many rows use the weight-streaming GEMM.
 constexpr int64_t SKINNY_MAX_M = 32;
@@ -26,6 +28,13 @@ int quantize_parts(int64_t M, int64_t K);
 hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora, int lora_parts,
                        const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
                        const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, void* y, hipStream_t stream);
+
+// MXFP4 GEMM (E8M0 scales per 32 columns; K % 128 == 0, N % 4 == 0; the activation scales
+// are (K/32, ms) with ms = M rounded up to 4) with the same fused epilogue.
+hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lora, int lora_parts,
+                          const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
+                          const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, int64_t ms, void* y,
+                          hipStream_t stream);
 
 // Weight-streaming variant for M <= SKINNY_MAX_M (called by launch_gemm).
 hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float* lora, int lora_parts,

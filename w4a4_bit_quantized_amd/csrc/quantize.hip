@@ -193,6 +193,36 @@ __device__ __forceinline__ void quantize_group(const float (&v)[16], const float
   codes = u32x2_t{nz ? w[0] : 0u, nz ? w[1] : 0u};
 }
 
+// MXFP4 block of 32 (rotate notes, section 3.3, FP-Quant mxfp4 / abs_max): the lane's 16 values
+// and those of lane l ^ 16 (the block's other half).  Scale 2^e with e the least exponent such
+// that 2^e >= float32(amax / 6), clamped to the E8M0 range [-127, 127]; the elements are
+// multiplied by the exact power of two 2^-e and rounded to E2M1.  Returns the 8 code bytes and
+// the E8M0 byte e + 127.  Every lane of the wave must call it (cross-lane exchange).
+__device__ __forceinline__ void quantize_block_mx(const float (&v)[16], u32x2_t& codes, uint32_t& e8) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t ab = __float_as_uint(amax);
+  const auto sw = __builtin_amdgcn_permlane16_swap(ab, ab, false, false);  // {own, partner} in some order
+  amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  const uint32_t qb = __float_as_uint(__fdiv_rn(amax, 6.0f));
+  const uint32_t ex = qb >> 23, mant = qb & 0x7FFFFFu;
+  // subnormal q = mant * 2^-149: above 2^-127 exactly when mant > 2^22
+  int e = ex == 0 ? (mant > 0x400000u ? -126 : -127) : (int)ex - 127 + (mant != 0u ? 1 : 0);
+  e = e > 127 ? 127 : e;
+  e8 = (uint32_t)(e + 127);
+  const float f = e == 127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = v[8 * h + i] * f;  // exact (a product below 2^-126 codes to 0 anyway)
+    w[h] = pack8(t);
+  }
+  codes = u32x2_t{w[0], w[1]};
+}
+
 // Raw input check for the fast x / lambda: every bf16 in `d` is +-0 or has
 // 2^-64 <= |x| < 2^96.  Accumulates packed u16 minima / maxima.
 __device__ __forceinline__ void range_acc(uint32_t d, u16x2_t& mn, u16x2_t& mx) {
@@ -205,10 +235,13 @@ __device__ __forceinline__ bool range_bad(u16x2_t mn, u16x2_t mx) {
   return (mn[0] < 0x1F7Fu) | (mn[1] < 0x1F7Fu) | (mx[0] >= 0x6F80u) | (mx[1] >= 0x6F80u);
 }
 
-template <int HB, bool ACT, int RB>
+// MX selects the MXFP4 blocks (32 columns, E8M0 scales in rows of `ms` bytes: the scale of
+// block b of row m is at scales[b * ms + m]; rows M .. ms - 1 receive 0) instead of the
+// 16-column e4m3 groups (scales[g * M + m]).
+template <int HB, bool ACT, int RB, bool MX>
 __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam, const uint16_t* __restrict__ pd,
-    int M, int K, int R, int units_per_wave, int nunits,
+    int M, int K, int R, int units_per_wave, int nunits, int ms,
     uint8_t* __restrict__ q, uint8_t* __restrict__ scales, float* __restrict__ lora) {
   using C = QCfg<HB, ACT, RB>;
   constexpr int US = C::US, UC = C::UC, RP = C::RP, RS = C::RS;
@@ -467,12 +500,16 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
       const int k0 = u * UC + 64 * c + 16 * qd;
       u32x2_t codes;
       uint32_t s8;
-      quantize_group(v[c], rtab, codes, s8);
+      if constexpr (MX) quantize_block_mx(v[c], codes, s8);
+      else quantize_group(v[c], rtab, codes, s8);
       if (row_ok && k0 < K) {
         uint32_t* qp = reinterpret_cast<uint32_t*>(qrow + (k0 >> 1));  // 4-byte aligned output
         qp[0] = codes[0];
         qp[1] = codes[1];
-        scales[(size_t)(k0 >> 4) * M + m] = (uint8_t)s8;
+        if constexpr (!MX) scales[(size_t)(k0 >> 4) * M + m] = (uint8_t)s8;
+      }
+      if constexpr (MX) {  // the block's even half stores its scale; padding rows store 0
+        if ((qd & 1) == 0 && m < ms && k0 < K) scales[(size_t)(k0 >> 5) * ms + m] = row_ok ? (uint8_t)s8 : (uint8_t)0;
       }
     }
   }
@@ -497,54 +534,62 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
   }
 }
 
-template <int HB, bool ACT, int RB>
-hipError_t launch_one(dim3 grid, int nunits, int per_part, hipStream_t st, const uint16_t* x, const uint16_t* lam,
-                      const uint16_t* pd, int M, int K, int R, uint8_t* q, uint8_t* sc, float* lora) {
+template <int HB, bool ACT, int RB, bool MX>
+hipError_t launch_one(dim3 grid, int nunits, int per_part, int ms, hipStream_t st, const uint16_t* x,
+                      const uint16_t* lam, const uint16_t* pd, int M, int K, int R, uint8_t* q, uint8_t* sc,
+                      float* lora) {
   using C = QCfg<HB, ACT, RB>;
   int nwaves = per_part < C::WAVES ? per_part : C::WAVES;
   if (nwaves < 1) nwaves = 1;
   const int upw = (per_part + nwaves - 1) / nwaves;
   nwaves = (per_part + upw - 1) / upw;
   if (nwaves < 1) nwaves = 1;
-  quantize_kernel<HB, ACT, RB><<<grid, dim3(64 * nwaves), 0, st>>>(x, lam, pd, M, K, R, upw, nunits, q, sc, lora);
+  quantize_kernel<HB, ACT, RB, MX><<<grid, dim3(64 * nwaves), 0, st>>>(x, lam, pd, M, K, R, upw, nunits, ms, q, sc,
+                                                                        lora);
   return hipGetLastError();
 }
 
-template <int HB, bool ACT>
-hipError_t launch_rb(int rb, dim3 grid, int nunits, int per_part, hipStream_t st, const uint16_t* x,
+#define W4A4_Q_ARGS grid, nunits, per_part, ms, st, x, lam, pd, M, K, R, q, sc, lora
+
+template <int HB, bool ACT, bool MX>
+hipError_t launch_rb(int rb, dim3 grid, int nunits, int per_part, int ms, hipStream_t st, const uint16_t* x,
                      const uint16_t* lam, const uint16_t* pd, int M, int K, int R, uint8_t* q, uint8_t* sc,
                      float* lora) {
-  switch (rb) {
-    case 0: return launch_one<HB, ACT, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-    case 1: return launch_one<HB, ACT, 1>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-    case 2: return launch_one<HB, ACT, 2>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-    case 3: return launch_one<HB, ACT, 3>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-    default: return launch_one<HB, ACT, 4>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+  if constexpr (!ACT) {
+    return launch_one<HB, false, 0, MX>(W4A4_Q_ARGS);
+  } else {
+    switch (rb) {
+      case 0: return launch_one<HB, true, 0, MX>(W4A4_Q_ARGS);
+      case 1: return launch_one<HB, true, 1, MX>(W4A4_Q_ARGS);
+      case 2: return launch_one<HB, true, 2, MX>(W4A4_Q_ARGS);
+      case 3: return launch_one<HB, true, 3, MX>(W4A4_Q_ARGS);
+      default: return launch_one<HB, true, 4, MX>(W4A4_Q_ARGS);
+    }
   }
 }
 
-template <bool ACT>
-hipError_t launch_hb(int hb, int rb, dim3 grid, int nunits, int per_part, hipStream_t st, const uint16_t* x,
+template <bool ACT, bool MX>
+hipError_t launch_hb(int hb, int rb, dim3 grid, int nunits, int per_part, int ms, hipStream_t st, const uint16_t* x,
                      const uint16_t* lam, const uint16_t* pd, int M, int K, int R, uint8_t* q, uint8_t* sc,
                      float* lora) {
-  if constexpr (ACT) {
+  if constexpr (MX) {  // the MX variant rotates in blocks of 32 or not at all
     switch (hb) {
-      case 0: return launch_rb<0, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-      case 16: return launch_rb<16, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-      case 32: return launch_rb<32, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-      case 64: return launch_rb<64, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-      default: return launch_rb<128, true>(rb, grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      case 0: return launch_rb<0, ACT, true>(rb, W4A4_Q_ARGS);
+      case 32: return launch_rb<32, ACT, true>(rb, W4A4_Q_ARGS);
+      default: return hipErrorInvalidValue;
     }
   } else {
     switch (hb) {
-      case 0: return launch_one<0, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-      case 16: return launch_one<16, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-      case 32: return launch_one<32, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-      case 64: return launch_one<64, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
-      default: return launch_one<128, false, 0>(grid, nunits, per_part, st, x, lam, pd, M, K, R, q, sc, lora);
+      case 0: return launch_rb<0, ACT, false>(rb, W4A4_Q_ARGS);
+      case 16: return launch_rb<16, ACT, false>(rb, W4A4_Q_ARGS);
+      case 32: return launch_rb<32, ACT, false>(rb, W4A4_Q_ARGS);
+      case 64: return launch_rb<64, ACT, false>(rb, W4A4_Q_ARGS);
+      default: return launch_rb<128, ACT, false>(rb, W4A4_Q_ARGS);
     }
   }
 }
+
+#undef W4A4_Q_ARGS
 
 }  // namespace
 
@@ -557,19 +602,27 @@ int quantize_parts(int64_t M, int64_t K) {
 }
 
 hipError_t launch_quantize(bool act, const void* x, const void* lam, const void* pd, int64_t M, int64_t K,
-                           int64_t R, int hb, int parts, void* q, void* scales, float* lora, hipStream_t stream) {
+                           int64_t R, int hb, int parts, void* q, void* scales, float* lora, hipStream_t stream,
+                           bool mx, int64_t scale_stride) {
   const int uc = hb == 128 ? 128 : 64;
   const int nunits = (int)((K + uc - 1) / uc);
   const int per_part = (nunits + parts - 1) / parts;
   const int rb = act ? (int)((R + 15) / 16) : 0;
+  const int ms = mx ? (int)scale_stride : (int)M;
   dim3 grid((unsigned)((M + QROWS - 1) / QROWS), (unsigned)parts);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* lp = static_cast<const uint16_t*>(lam);
   const uint16_t* pp = static_cast<const uint16_t*>(pd);
   uint8_t* qp = static_cast<uint8_t*>(q);
   uint8_t* sp = static_cast<uint8_t*>(scales);
-  if (act) return launch_hb<true>(hb, rb, grid, nunits, per_part, stream, xp, lp, pp, (int)M, (int)K, (int)R, qp, sp, lora);
-  return launch_hb<false>(hb, 0, grid, nunits, per_part, stream, xp, lp, pp, (int)M, (int)K, 0, qp, sp, nullptr);
+  const int r = act ? (int)R : 0;
+  float* lo = act ? lora : nullptr;
+  if (act) {
+    if (mx) return launch_hb<true, true>(hb, rb, grid, nunits, per_part, ms, stream, xp, lp, pp, (int)M, (int)K, r, qp, sp, lo);
+    return launch_hb<true, false>(hb, rb, grid, nunits, per_part, ms, stream, xp, lp, pp, (int)M, (int)K, r, qp, sp, lo);
+  }
+  if (mx) return launch_hb<false, true>(hb, 0, grid, nunits, per_part, ms, stream, xp, lp, pp, (int)M, (int)K, 0, qp, sp, lo);
+  return launch_hb<false, false>(hb, 0, grid, nunits, per_part, ms, stream, xp, lp, pp, (int)M, (int)K, 0, qp, sp, lo);
 }
 
 }  // namespace w4a4

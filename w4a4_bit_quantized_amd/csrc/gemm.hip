@@ -45,6 +45,23 @@ namespace {
 constexpr int BK = 128;            // K columns per stage (8 groups of 16)
 constexpr int CODE_STRIDE = 80;    // LDS bytes per code row: 64 data + 16 pad (conflict-free b128 reads)
 
+// Output tile (tm, tn) of workgroup b among G tiles of a tiles_m x tiles_n grid.  Workgroups are
+// dispatched to the 8 XCDs in turn; each XCD takes a contiguous range of a grouped order that
+// walks GROUP_M tile rows column by column, so the tiles one XCD runs at a time share a few
+// activation and weight panels in its L2.
+constexpr int GROUP_M = 8;
+
+__device__ __forceinline__ void tile_of(int b, int G, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int q = G / 8, r = G % 8, x = b % 8, l = b / 8;
+  const int p = x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;  // position in the grouped order
+  const int group = p / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int rows = min(GROUP_M, tiles_m - first_m);
+  const int in = p - group * GROUP_M * tiles_n;
+  tm = first_m + in % rows;
+  tn = in / rows;
+}
+
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 struct Tile {
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
@@ -405,8 +422,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int l32 = lane & 31, h = lane >> 5;
   const int tiles_n = (N + T::BN - 1) / T::BN;
-  const int n0 = (int)(blockIdx.x % tiles_n) * T::BN;
-  const int m0 = (int)(blockIdx.x / tiles_n) * T::BM;
+  int tm, tn;
+  tile_of((int)blockIdx.x, (int)gridDim.x, (M + T::BM - 1) / T::BM, tiles_n, tm, tn);
+  const int n0 = tn * T::BN;
+  const int m0 = tm * T::BM;
   const int kbytes = K / 2;
   const int groups = K / 16;
   const int nkt = (K + BK - 1) / BK;
@@ -478,13 +497,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 // computed, so two K-steps of latency are covered and the only waits are the explicit ones
 // ahead of each barrier.
 //  * Codes: each wave instruction (dwordx4) fills 1 KB = 16 rows of 64 bytes.  Chunk c of row r
-//    is placed at 16-byte position c ^ ((r >> 1) & 3), which keeps the operand reads of 8
-//    consecutive rows on distinct banks.
+//    is placed at 16-byte position c ^ code_swizzle(r), which keeps the operand reads of 16
+//    consecutive rows (one pass of a 16-byte LDS read) on distinct banks.
 //  * Scales: each lane moves one dword of the (K/16, rows) scale tensor (4 consecutive rows of
 //    one group); the dwords are laid out [row quad][8 groups], so a lane reads the 4 groups of
 //    its half with one 16-byte read and picks its row's byte out of each dword.
 // Rows past the tile's valid ones (and the padding up to whole instructions) read clamped
 // valid rows and are never stored.
+// 16-byte chunk position of a code row's chunk 0 in LDS (chunk c goes to c ^ code_swizzle(r)):
+// rows r and r + 4 share banks (64-byte rows, 256 bytes of banks), so the four rows of a bank
+// line take distinct positions.
+__device__ __forceinline__ int code_swizzle(int row) { return (row >> 2) & 3; }
+
 template <class T>
 struct DmaTile {
   static constexpr int WAVES = T::WM * T::WN;
@@ -543,8 +567,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int l32 = lane & 31, h = lane >> 5;
   const int tiles_n = (N + T::BN - 1) / T::BN;
-  const int n0 = (int)(blockIdx.x % tiles_n) * T::BN;
-  const int m0 = (int)(blockIdx.x / tiles_n) * T::BM;
+  int tm, tn;
+  tile_of((int)blockIdx.x, (int)gridDim.x, (M + T::BM - 1) / T::BM, tiles_n, tm, tn);
+  const int n0 = tn * T::BN;
+  const int m0 = tm * T::BM;
   const uint32_t kbytes = (uint32_t)K / 2;
   const int nkt = K / BK;
   const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);  // multiples of 4
@@ -555,7 +581,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 #pragma unroll
   for (int r = 0; r < D::ROUNDS; ++r) {
     const int row = r * D::ROUND_ROWS + wave * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const int c = (lane & 3) ^ code_swizzle(row);
     const bool is_a = row < T::BM;
     const int src = is_a ? min(row, rows_a - 1) : min(row - T::BM, rows_b - 1);
     c_base[r] = is_a ? qa + (size_t)m0 * kbytes : qw + (size_t)n0 * kbytes;
@@ -612,7 +638,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm * FM * 32 + i * 32 + l32;
-      const int sw4 = (row >> 1) & 3;
+      const int sw4 = code_swizzle(row);
       scales_of(cur, row, sA[i]);
       cA[0][i] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h) ^ sw4));
       cA[1][i] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h + 1) ^ sw4));
@@ -620,7 +646,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = T::BM + wn * FN * 32 + j * 32 + l32;
-      const int sw4 = (row >> 1) & 3;
+      const int sw4 = code_swizzle(row);
       scales_of(cur, row, sB[j]);
       cB[0][j] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h) ^ sw4));
       cB[1][j] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h + 1) ^ sw4));
@@ -645,8 +671,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 // A K-step of 128 columns is two instructions; lane half h reads code chunks h and 2 + h of
 // its row and the scales of blocks h and 2 + h.  The accumulator layout equals the f16
 // kernel's, so the epilogue is shared.
-template <class T>
+template <class T, int S>
 struct DmaTileMx {
+  static constexpr int STAGES = S;                // K-steps resident in LDS; S - 1 of them in flight
   static constexpr int WAVES = T::WM * T::WN;
   static constexpr int ROUND_ROWS = 16 * WAVES;
   static constexpr int ROUNDS = (T::ROWS + ROUND_ROWS - 1) / ROUND_ROWS;
@@ -655,22 +682,23 @@ struct DmaTileMx {
   static constexpr int SCALE_OFF = ROUNDS * ROUND_ROWS * 64;
   static constexpr int STAGE = SCALE_OFF + SROUNDS * WAVES * 256;
   static constexpr int LOADS = ROUNDS + SROUNDS;
-  static constexpr int LDS_BYTES = 3 * STAGE > T::EPI_BYTES ? 3 * STAGE : T::EPI_BYTES;
+  static constexpr int LDS_BYTES = S * STAGE > T::EPI_BYTES ? S * STAGE : T::EPI_BYTES;
   static_assert(T::BM % 16 == 0 && T::ROWS % 16 == 0, "whole 16-row blocks");
+  static_assert(S >= 3 && (S - 2) * LOADS < 64, "vmcnt range");
 };
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // `ms` is the row stride of the activation scale tensor (M rounded up to 4).
-template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
+template <int WAVES_M, int WAVES_N, int FM, int FN, int S, bool LORA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
     const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R, int ms,
     uint16_t* __restrict__ y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
-  using D = DmaTileMx<T>;
+  using D = DmaTileMx<T, S>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[D::LDS_BYTES];
 
   const int t = threadIdx.x;
@@ -679,8 +707,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int l32 = lane & 31, h = lane >> 5;
   const int tiles_n = (N + T::BN - 1) / T::BN;
-  const int n0 = (int)(blockIdx.x % tiles_n) * T::BN;
-  const int m0 = (int)(blockIdx.x / tiles_n) * T::BM;
+  int tm, tn;
+  tile_of((int)blockIdx.x, (int)gridDim.x, (M + T::BM - 1) / T::BM, tiles_n, tm, tn);
+  const int n0 = tn * T::BN;
+  const int m0 = tm * T::BM;
   const uint32_t kbytes = (uint32_t)K / 2;
   const int nkt = K / BK;
   const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);
@@ -691,7 +721,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
 #pragma unroll
   for (int r = 0; r < D::ROUNDS; ++r) {
     const int row = r * D::ROUND_ROWS + wave * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const int c = (lane & 3) ^ code_swizzle(row);
     const bool is_a = row < T::BM;
     const int src = is_a ? min(row, rows_a - 1) : min(row - T::BM, rows_b - 1);
     c_base[r] = is_a ? qa + (size_t)m0 * kbytes : qw + (size_t)n0 * kbytes;
@@ -711,11 +741,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
     s_off[r] = (uint32_t)g * s_stride[r] + (uint32_t)row;
   }
 
-  // K-step kt covers 4 scale blocks: block rows 4 kt .. 4 kt + 3 of the scale tensors
-  dma_issue<D>(lds, wave, 0u, (size_t)0, c_base, c_off, s_base, s_off, s_stride);
-  dma_issue<D>(lds + D::STAGE, wave, (uint32_t)(nkt > 1 ? 1 : 0) * (BK / 2), (size_t)(nkt > 1 ? 1 : 0) * (BK / 32),
-               c_base, c_off, s_base, s_off, s_stride);
-  vm_wait_barrier<0>();
+  // K-step kt covers 4 scale blocks: block rows 4 kt .. 4 kt + 3 of the scale tensors.  The first
+  // S - 1 K-steps are issued up front (past the last one, the last is reloaded).
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) {
+    const int kj = min(j, nkt - 1);
+    dma_issue<D>(lds + j * D::STAGE, wave, (uint32_t)kj * (BK / 2), (size_t)kj * (BK / 32), c_base, c_off, s_base,
+                 s_off, s_stride);
+  }
+  vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step 0 has landed
 
   float16_t acc[FM][FN];
 #pragma unroll
@@ -730,8 +764,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
   const uint32_t psel = (uint32_t)(l32 & 3) | ((uint32_t)(4 + (l32 & 3)) << 8) | 0x0C0C0000u;
   int slot = 0;
   for (int kt = 0; kt < nkt; ++kt) {
-    const int slot2 = slot == 0 ? 2 : slot - 1;
-    const int kn = min(kt + 2, nkt - 1);
+    const int slot2 = slot == 0 ? S - 1 : slot - 1;  // (kt + S - 1) % S: read in K-step kt - 1, now free
+    const int kn = min(kt + S - 1, nkt - 1);
     dma_issue<D>(lds + slot2 * D::STAGE, wave, (uint32_t)kn * (BK / 2), (size_t)kn * (BK / 32), c_base, c_off, s_base,
                  s_off, s_stride);
     const uint8_t* cur = lds + slot * D::STAGE;
@@ -740,7 +774,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm * FM * 32 + i * 32 + l32;
-      const int sw4 = (row >> 1) & 3;
+      const int sw4 = code_swizzle(row);
       const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
       sA[i] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
 #pragma unroll
@@ -752,7 +786,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = T::BM + wn * FN * 32 + j * 32 + l32;
-      const int sw4 = (row >> 1) & 3;
+      const int sw4 = code_swizzle(row);
       const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
       sB[j] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
 #pragma unroll
@@ -771,15 +805,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cB[1][j], cA[1][i], acc[i][j], 4, 4, 1, sB[j], 1,
                                                                     sA[i]);
       }
-    vm_wait_barrier<D::LOADS>();
-    slot = slot == 2 ? 0 : slot + 1;
+    vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step kt + 1 has landed
+    slot = slot == S - 1 ? 0 : slot + 1;
   }
   vm_wait_barrier<0>();
 
   epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
 }
 
-template <int WAVES_M, int WAVES_N, int FM, int FN>
+template <int WAVES_M, int WAVES_N, int FM, int FN, int S = 3>
 hipError_t launch_mx_tile(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                           const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
                           const uint16_t* wts, int M, int N, int K, int R, int ms, uint16_t* y) {
@@ -787,9 +821,9 @@ hipError_t launch_mx_tile(int rb, hipStream_t st, const uint8_t* qa, const uint8
   dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
   dim3 block(T::THREADS);
   if (rb > 0)
-    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
+    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
   else
-    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
+    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
   return hipGetLastError();
 }
 

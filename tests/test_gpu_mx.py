@@ -110,7 +110,7 @@ def test_gemm_lowrank_mx_parity(w4, M, N, K, R):
     _check_gemm_mx(w4, _lay(M, K, N, R, 32, seed=M * 7 + N))
 
 
-@pytest.mark.parametrize("tile", ["2x4x4x2", "2x2x2x2"])
+@pytest.mark.parametrize("tile", ["4x4x2x2", "2x4x4x2", "2x2x2x2"])
 def test_gemm_mx_each_tile(w4, tile, monkeypatch):
     monkeypatch.setenv("W4A4_GEMM_TILE", tile)
     _check_gemm_mx(w4, _lay(300, 640, 520, 32, 0, seed=41))

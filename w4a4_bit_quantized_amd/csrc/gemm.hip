@@ -379,6 +379,44 @@ __device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N],
       }
     }
   }
+  if ((N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+    // Coalesced stores: each wave passes its rounded tile through a private LDS region (IC fragment
+    // rows at a time) and writes whole 16-byte runs of y rows (a wave instruction covers
+    // 64 / CPR rows x 64 FN contiguous bytes).  Chunk ch of region row r sits at position
+    // (ch + r / 2) % CPR, which keeps both the 8-byte writes and the 16-byte reads on distinct banks.
+    constexpr int WAVES = T::WM * T::WN;
+    constexpr int RSB = FN * 64;  // bytes per region row
+    constexpr int CPR = FN * 4;   // 16-byte chunks per region row
+    constexpr int IC = WAVES * FM * 32 * RSB <= T::EPI_BYTES ? FM
+                       : ((FM % 2) == 0 && WAVES * (FM / 2) * 32 * RSB <= T::EPI_BYTES) ? FM / 2 : 1;
+    static_assert(WAVES * IC * 32 * RSB <= T::EPI_BYTES, "store regions fit the epilogue's LDS");
+    __syncthreads();  // every wave is done with the staged operands
+    uint8_t* reg = lds + wave * IC * 32 * RSB;
+#pragma unroll
+    for (int i0 = 0; i0 < FM; i0 += IC) {
+#pragma unroll
+      for (int i = i0; i < i0 + IC; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = (i - i0) * 32 + l32, ch = 4 * j + q;
+            const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<u32x2_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR) + 8 * h) = u32x2_t{p0, p1};
+          }
+      wave_lds_sync();
+#pragma unroll
+      for (int it = 0; it < IC * CPR / 2; ++it) {
+        const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR));
+        const int m = mb + i0 * 32 + r, n = nb + 8 * ch;
+        if (m < M && n < N) *reinterpret_cast<u32x4_t*>(y + (size_t)m * N + n) = v;
+      }
+      wave_lds_sync();  // the region is rewritten by the next fragment rows
+    }
+    return;
+  }
   const bool n4 = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -959,11 +997,14 @@ hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lo
   auto wt = static_cast<const uint16_t*>(wtscale);
   auto yp = static_cast<uint16_t*>(y);
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R, s = (int)ms;
-  // 8-wave 256 x 256 tiles when they fill the chip, else 4-wave 128 x 128; W4A4_GEMM_TILE=2x4x4x2 or
-  // 2x2x2x2 forces one
+  // 16-wave 256 x 256 tiles (each wave 64 x 64: four waves per SIMD hide each other's scale
+  // permutes, LDS reads and barrier waits) when they fill the chip, else 4-wave 128 x 128;
+  // W4A4_GEMM_TILE=4x4x2x2, 2x4x4x2 (8 waves of 128 x 64) or 2x2x2x2 forces one
   const char* forced = getenv("W4A4_GEMM_TILE");
-  const bool big = forced ? !strcmp(forced, "2x4x4x2") : tile_score(M, N, 256, 256) >= tile_score(M, N, 128, 128);
-  if (big) return launch_mx_tile<2, 4, 4, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
+  const bool big = forced ? !strcmp(forced, "4x4x2x2") : tile_score(M, N, 256, 256) >= tile_score(M, N, 128, 128);
+  if (forced && !strcmp(forced, "2x4x4x2"))
+    return launch_mx_tile<2, 4, 4, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
+  if (big) return launch_mx_tile<4, 4, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
   return launch_mx_tile<2, 2, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
 }
 

@@ -110,10 +110,22 @@ def test_gemm_lowrank_mx_parity(w4, M, N, K, R):
     _check_gemm_mx(w4, _lay(M, K, N, R, 32, seed=M * 7 + N))
 
 
-@pytest.mark.parametrize("tile", ["4x4x2x2", "2x4x4x2", "2x2x2x2"])
-def test_gemm_mx_each_tile(w4, tile, monkeypatch):
+@pytest.mark.parametrize("tile", ["4x4x2x2", "2x4x4x2", "2x2x2x2", "2x2x4x4"])
+@pytest.mark.parametrize("N", [520, 516])
+def test_gemm_mx_each_tile(w4, tile, N, monkeypatch):
+    """Each MX tile layout (2x2x4x4: one wave per SIMD with register prefetch)
+    on a ragged shape with an odd number of K-steps, with y rows that are whole 16-byte runs
+    (N = 520) and that are not (N = 516)."""
     monkeypatch.setenv("W4A4_GEMM_TILE", tile)
-    _check_gemm_mx(w4, _lay(300, 640, 520, 32, 0, seed=41))
+    _check_gemm_mx(w4, _lay(300, 640, N, 32, 0, seed=41))
+
+
+@pytest.mark.parametrize("tile", ["4x4x2x2", "2x2x4x4"])
+@pytest.mark.parametrize("K", [128, 256, 384])
+def test_gemm_mx_few_k_steps(w4, tile, K, monkeypatch):
+    """Fewer K-steps than pipeline stages."""
+    monkeypatch.setenv("W4A4_GEMM_TILE", tile)
+    _check_gemm_mx(w4, _lay(260, K, 264, 16, 0, seed=K))
 
 
 @pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 32), (37, 68, 384, 16, 0), (16, 200, 2048, 32, 32),

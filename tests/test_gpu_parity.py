@@ -167,6 +167,17 @@ def test_gemm_every_tile_variant(w4, variant, path, monkeypatch):
     _check_gemm(w4, lay)
 
 
+@pytest.mark.parametrize("variant,path,N", [("2x2x4x4", "dma", 516), ("2x2x4x4", "stage", 518),
+                                            ("2x4x4x2", "stage", 518), ("2x2x2x2", "dma", 516)])
+def test_gemm_tile_unaligned_rows(w4, variant, path, N, monkeypatch):
+    """y rows that are not whole 16-byte runs leave the epilogue by direct stores (8-byte runs for
+    N % 4 == 0, single values otherwise), in both the fragment-row-wise and the whole-tile epilogue."""
+    monkeypatch.setenv("W4A4_GEMM_TILE", variant)
+    monkeypatch.setenv("W4A4_GEMM_PATH", path)
+    lay = synth.make_layer("tiny", seed=N, M=300, K=640, N=N, R=32, B=0, wcs="uniform")
+    _check_gemm(w4, lay)
+
+
 @pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 0), (37, 70, 256, 32, 128), (3, 40, 48, 3, 16),
                                        (150, 260, 512, 64, 64),
                                        # small batches: K split across quantizer workgroups (partial low-rank sums)

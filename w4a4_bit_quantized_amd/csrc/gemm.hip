@@ -78,7 +78,12 @@ struct Tile {
   // Epilogue operands, staged in the stage buffers after the K loop: L hi and lo parts
   // [BM][64] bf16, proj_up [BN][64] bf16 and the column scale [BN] f32.
   static constexpr int EPI_BYTES = BM * 64 * 2 * 2 + BN * 64 * 2 + BN * 4;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_BYTES ? 2 * STAGE_BYTES : EPI_BYTES;
+  // Waves with 16 or more accumulator fragments (which fill the accumulation registers) finish
+  // one fragment row at a time, each wave through a 32-row store region of its own placed after
+  // the epilogue operands.
+  static constexpr bool ROWWISE = FM * FN >= 16;
+  static constexpr int EPI_LDS = EPI_BYTES + (ROWWISE ? WAVES_M * WAVES_N * 32 * FN * 64 : 0);
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_LDS ? 2 * STAGE_BYTES : EPI_LDS;
 };
 
 // Stage a tile's epilogue operands in LDS: the column scales wcscales * wtscale, and for the
@@ -350,6 +355,72 @@ __device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N],
   const uint16_t* l_lo = l_hi + T::BM * rs;
   const uint16_t* p_lds = l_lo + T::BM * rs;
   const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
+  if constexpr (T::ROWWISE) {
+    // Same arithmetic, in the same order per element, one fragment at a time; each fragment
+    // row then leaves through the wave's store region (16-byte stores) or, when y rows are not
+    // whole 16-byte runs, directly.
+    constexpr int RSB = FN * 64, CPR = FN * 4;
+    uint8_t* reg = lds + T::EPI_BYTES + wave * 32 * RSB;
+    const bool coalesce = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    const bool n4 = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * FM * 32 + i * 32 + l32;
+      const int m = mb + i * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float16_t a = acc[i][j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[4 * q + e] *= c[e];
+        }
+        if (LORA) {
+          for (int r0 = 0; r0 < rp; r0 += 16) {
+            const bf16x8_t pv =
+                *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * rs + r0 + 8 * h);
+            const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * rs + r0 + 8 * h);
+            const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
+            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv, lhi, a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv, llo, a, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t p0 = pack_bf16x2(a[4 * q], a[4 * q + 1]);
+          const uint32_t p1 = pack_bf16x2(a[4 * q + 2], a[4 * q + 3]);
+          const int n = nb + j * 32 + 8 * q + 4 * h;
+          if (coalesce) {
+            const int ch = 4 * j + q;
+            *reinterpret_cast<u32x2_t*>(reg + l32 * RSB + 16 * ((ch + (l32 >> 1)) % CPR) + 8 * h) = u32x2_t{p0, p1};
+          } else if (m < M) {
+            uint16_t* yrow = y + (size_t)m * N;
+            if (n4) {
+              if (n < N) *reinterpret_cast<u32x2_t*>(yrow + n) = u32x2_t{p0, p1};
+            } else {
+              const uint16_t v[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (n + e < N) yrow[n + e] = v[e];
+            }
+          }
+        }
+      }
+      if (coalesce) {
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < CPR / 2; ++it) {
+          const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR));
+          const int mr = mb + i * 32 + r, n = nb + 8 * ch;
+          if (mr < M && n < N) *reinterpret_cast<u32x4_t*>(y + (size_t)mr * N + n) = v;
+        }
+        wave_lds_sync();  // the region is rewritten by the next fragment row
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -557,7 +628,7 @@ struct DmaTile {
   static constexpr int SCALE_OFF = ROUNDS * ROUND_ROWS * 64;
   static constexpr int STAGE = SCALE_OFF + SROUNDS * WAVES * 256;
   static constexpr int LOADS = ROUNDS + SROUNDS;  // load instructions per wave per K-step
-  static constexpr int LDS_BYTES = 3 * STAGE > T::EPI_BYTES ? 3 * STAGE : T::EPI_BYTES;
+  static constexpr int LDS_BYTES = 3 * STAGE > T::EPI_LDS ? 3 * STAGE : T::EPI_LDS;
   static_assert(T::BM % 16 == 0 && T::ROWS % 16 == 0, "whole 16-row blocks");
 };
 
@@ -720,7 +791,7 @@ struct DmaTileMx {
   static constexpr int SCALE_OFF = ROUNDS * ROUND_ROWS * 64;
   static constexpr int STAGE = SCALE_OFF + SROUNDS * WAVES * 256;
   static constexpr int LOADS = ROUNDS + SROUNDS;
-  static constexpr int LDS_BYTES = S * STAGE > T::EPI_BYTES ? S * STAGE : T::EPI_BYTES;
+  static constexpr int LDS_BYTES = S * STAGE > T::EPI_LDS ? S * STAGE : T::EPI_LDS;
   static_assert(T::BM % 16 == 0 && T::ROWS % 16 == 0, "whole 16-row blocks");
   static_assert(S >= 3 && (S - 2) * LOADS < 64, "vmcnt range");
 };
@@ -728,8 +799,128 @@ struct DmaTileMx {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// `ms` is the row stride of the activation scale tensor (M rounded up to 4).
-template <int WAVES_M, int WAVES_N, int FM, int FN, int S, bool LORA>
+// Read a wave's operands of one K-step from its LDS stage: per fragment the scale register
+// (byte 0: block h, byte 1: block 2 + h of the lane's row) and the two instructions' code chunks.
+template <class T, class D>
+__device__ __forceinline__ void mx_read(const uint8_t* cur, int wm, int wn, int l32, int h, uint32_t psel,
+                                        uint32_t (&sA)[T::FRAG_M], uint32_t (&sB)[T::FRAG_N],
+                                        i32x4_t (&cA)[2][T::FRAG_M], i32x4_t (&cB)[2][T::FRAG_N]) {
+#pragma unroll
+  for (int i = 0; i < T::FRAG_M; ++i) {
+    const int row = wm * T::FRAG_M * 32 + i * 32 + l32;
+    const int sw4 = code_swizzle(row);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+    sA[i] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < T::FRAG_N; ++j) {
+    const int row = T::BM + wn * T::FRAG_N * 32 + j * 32 + l32;
+    const int sw4 = code_swizzle(row);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+    sB[j] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
+    }
+  }
+}
+
+// As mx_read, but the scale dwords are kept as read (two per fragment: blocks h and 2 + h) and
+// combined only where they are used, so that no LDS wait falls between the matrix instructions.
+template <class T, class D>
+__device__ __forceinline__ void mx_read_raw(const uint8_t* cur, int wm, int wn, int l32, int h,
+                                            uint32_t (&qA)[T::FRAG_M][2], uint32_t (&qB)[T::FRAG_N][2],
+                                            i32x4_t (&cA)[2][T::FRAG_M], i32x4_t (&cB)[2][T::FRAG_N]) {
+#pragma unroll
+  for (int i = 0; i < T::FRAG_M; ++i) {
+    const int row = wm * T::FRAG_M * 32 + i * 32 + l32;
+    const int sw4 = code_swizzle(row);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+    qA[i][0] = sq[h];
+    qA[i][1] = sq[2 + h];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
+  }
+#pragma unroll
+  for (int j = 0; j < T::FRAG_N; ++j) {
+    const int row = T::BM + wn * T::FRAG_N * 32 + j * 32 + l32;
+    const int sw4 = code_swizzle(row);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+    qB[j][0] = sq[h];
+    qB[j][1] = sq[2 + h];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
+  }
+}
+
+// One K-step on the matrix cores: weights first (output columns n), activations second (output
+// rows m), as in the f16 kernel.
+template <int FM, int FN>
+__device__ __forceinline__ void mx_mma(float16_t (&acc)[FM][FN], const uint32_t (&sA)[FM], const uint32_t (&sB)[FN],
+                                       const i32x4_t (&cA)[2][FM], const i32x4_t (&cB)[2][FN]) {
+  // FP4 operands occupy the first four registers of the instruction's eight
+  auto w = [](i32x4_t c) { return __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1); };
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w(cB[0][j]), w(cA[0][i]), acc[i][j], 4, 4, 0, sB[j], 0,
+                                                                  sA[i]);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w(cB[1][j]), w(cA[1][i]), acc[i][j], 4, 4, 1, sB[j], 1,
+                                                                  sA[i]);
+}
+
+// K-step kt of the register-prefetching loop: operands of kt are in (qA, qB, cA, cB); those of
+// kt + 1 are read into (nA, nB, dA, dB) while kt multiplies.  Once every wave holds K-step kt in
+// registers, its slot `sl` = kt % S is refilled with K-step kt + S.  Past the last K-step the
+// last one is reloaded and re-read, so every step issues the same loads (uniform vmcnt) and
+// runs without branches.  The matrix instructions are interleaved with the LDS reads and the
+// direct loads (one wave per SIMD: nothing else fills the matrix pipe while this wave stalls).
+template <class T, class D, int S>
+__device__ __forceinline__ void mx_pf_step(int kt, int sl, int nkt, uint8_t* lds,
+                                           float16_t (&acc)[T::FRAG_M][T::FRAG_N], int wave, int wm, int wn, int l32,
+                                           int h, uint32_t psel, const uint8_t* const* c_base, const uint32_t* c_off,
+                                           const uint8_t* const* s_base, const uint32_t* s_off,
+                                           const uint32_t* s_stride, const uint32_t (&qA)[T::FRAG_M][2],
+                                           const uint32_t (&qB)[T::FRAG_N][2], const i32x4_t (&cA)[2][T::FRAG_M],
+                                           const i32x4_t (&cB)[2][T::FRAG_N], uint32_t (&nA)[T::FRAG_M][2],
+                                           uint32_t (&nB)[T::FRAG_N][2], i32x4_t (&dA)[2][T::FRAG_M],
+                                           i32x4_t (&dB)[2][T::FRAG_N]) {
+  constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
+  vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step kt + 1 has landed
+  uint32_t sA[FM], sB[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) sA[i] = __builtin_amdgcn_perm(qA[i][1], qA[i][0], psel);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) sB[j] = __builtin_amdgcn_perm(qB[j][1], qB[j][0], psel);
+  const int kn = min(kt + S, nkt - 1);
+  dma_issue<D>(lds + sl * D::STAGE, wave, (uint32_t)kn * (BK / 2), (size_t)kn * (BK / 32), c_base, c_off, s_base,
+               s_off, s_stride);
+  const int sn = sl == S - 1 ? 0 : sl + 1;
+  mx_read_raw<T, D>(lds + sn * D::STAGE, wm, wn, l32, h, nA, nB, dA, dB);
+  mx_mma(acc, sA, sB, cA, cB);
+  // per matrix instruction of the first 2 (FM + FN): two LDS reads and one direct load
+#pragma unroll
+  for (int g = 0; g < 2 * (FM + FN); ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // vector memory read
+  }
+}
+
+// `ms` is the row stride of the activation scale tensor (M rounded up to 4).  PF selects the
+// register-prefetching K loop (for one wave per SIMD, whose LDS latency no other wave hides).
+template <int WAVES_M, int WAVES_N, int FM, int FN, int S, bool PF, bool LORA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
@@ -779,16 +970,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
     s_off[r] = (uint32_t)g * s_stride[r] + (uint32_t)row;
   }
 
-  // K-step kt covers 4 scale blocks: block rows 4 kt .. 4 kt + 3 of the scale tensors.  The first
-  // S - 1 K-steps are issued up front (past the last one, the last is reloaded).
-#pragma unroll
-  for (int j = 0; j < S - 1; ++j) {
-    const int kj = min(j, nkt - 1);
-    dma_issue<D>(lds + j * D::STAGE, wave, (uint32_t)kj * (BK / 2), (size_t)kj * (BK / 32), c_base, c_off, s_base,
-                 s_off, s_stride);
-  }
-  vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step 0 has landed
-
   float16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -800,49 +981,56 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
   // byte of the lane's row in a scale dword: result byte 0 from the block-h dword, byte 1 from
   // the block-(2 + h) dword
   const uint32_t psel = (uint32_t)(l32 & 3) | ((uint32_t)(4 + (l32 & 3)) << 8) | 0x0C0C0000u;
+
+  // K-step kt covers 4 scale blocks: block rows 4 kt .. 4 kt + 3 of the scale tensors.
+  if constexpr (PF) {
+    static_assert((S - 1) * D::LOADS < 64, "vmcnt range");
+    // K-steps 0 .. S - 1 fill every slot up front (the last K-step repeated where there are fewer)
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int kj = min(j, nkt - 1);
+      dma_issue<D>(lds + j * D::STAGE, wave, (uint32_t)kj * (BK / 2), (size_t)kj * (BK / 32), c_base, c_off, s_base,
+                   s_off, s_stride);
+    }
+    vm_wait_barrier<(S - 1) * D::LOADS>();  // K-step 0 has landed
+    uint32_t sA0[FM][2], sB0[FN][2], sA1[FM][2], sB1[FN][2];
+    i32x4_t cA0[2][FM], cB0[2][FN], cA1[2][FM], cB1[2][FN];
+    mx_read_raw<T, D>(lds, wm, wn, l32, h, sA0, sB0, cA0, cB0);
+    int kt = 0, sl = 0;
+    for (; kt + 1 < nkt; kt += 2) {
+      mx_pf_step<T, D, S>(kt, sl, nkt, lds, acc, wave, wm, wn, l32, h, psel, c_base, c_off, s_base, s_off, s_stride,
+                          sA0, sB0, cA0, cB0, sA1, sB1, cA1, cB1);
+      sl = sl == S - 1 ? 0 : sl + 1;
+      mx_pf_step<T, D, S>(kt + 1, sl, nkt, lds, acc, wave, wm, wn, l32, h, psel, c_base, c_off, s_base, s_off,
+                          s_stride, sA1, sB1, cA1, cB1, sA0, sB0, cA0, cB0);
+      sl = sl == S - 1 ? 0 : sl + 1;
+    }
+    if (kt < nkt)
+      mx_pf_step<T, D, S>(kt, sl, nkt, lds, acc, wave, wm, wn, l32, h, psel, c_base, c_off, s_base, s_off, s_stride,
+                          sA0, sB0, cA0, cB0, sA1, sB1, cA1, cB1);
+    vm_wait_barrier<0>();
+    epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
+    return;
+  }
+
+  // The first S - 1 K-steps are issued up front (past the last one, the last is reloaded).
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) {
+    const int kj = min(j, nkt - 1);
+    dma_issue<D>(lds + j * D::STAGE, wave, (uint32_t)kj * (BK / 2), (size_t)kj * (BK / 32), c_base, c_off, s_base,
+                 s_off, s_stride);
+  }
+  vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step 0 has landed
   int slot = 0;
   for (int kt = 0; kt < nkt; ++kt) {
     const int slot2 = slot == 0 ? S - 1 : slot - 1;  // (kt + S - 1) % S: read in K-step kt - 1, now free
     const int kn = min(kt + S - 1, nkt - 1);
     dma_issue<D>(lds + slot2 * D::STAGE, wave, (uint32_t)kn * (BK / 2), (size_t)kn * (BK / 32), c_base, c_off, s_base,
                  s_off, s_stride);
-    const uint8_t* cur = lds + slot * D::STAGE;
     uint32_t sA[FM], sB[FN];
-    i32x8_t cA[2][FM], cB[2][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = wm * FM * 32 + i * 32 + l32;
-      const int sw4 = code_swizzle(row);
-      const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
-      sA[i] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const i32x4_t c = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
-        cA[s2][i] = __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1);  // upper half unread for FP4
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = T::BM + wn * FN * 32 + j * 32 + l32;
-      const int sw4 = code_swizzle(row);
-      const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
-      sB[j] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const i32x4_t c = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
-        cB[s2][j] = __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1);
-      }
-    }
-    // weights first (output columns n), activations second (output rows m), as in the f16 kernel
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cB[0][j], cA[0][i], acc[i][j], 4, 4, 0, sB[j], 0,
-                                                                    sA[i]);
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cB[1][j], cA[1][i], acc[i][j], 4, 4, 1, sB[j], 1,
-                                                                    sA[i]);
-      }
+    i32x4_t cA[2][FM], cB[2][FN];
+    mx_read<T, D>(lds + slot * D::STAGE, wm, wn, l32, h, psel, sA, sB, cA, cB);
+    mx_mma(acc, sA, sB, cA, cB);
     vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step kt + 1 has landed
     slot = slot == S - 1 ? 0 : slot + 1;
   }
@@ -851,7 +1039,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
   epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
 }
 
-template <int WAVES_M, int WAVES_N, int FM, int FN, int S = 3>
+template <int WAVES_M, int WAVES_N, int FM, int FN, int S = 3, bool PF = false>
 hipError_t launch_mx_tile(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                           const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
                           const uint16_t* wts, int M, int N, int K, int R, int ms, uint16_t* y) {
@@ -859,9 +1047,9 @@ hipError_t launch_mx_tile(int rb, hipStream_t st, const uint8_t* qa, const uint8
   dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
   dim3 block(T::THREADS);
   if (rb > 0)
-    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
+    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, PF, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
   else
-    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
+    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, PF, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
   return hipGetLastError();
 }
 
@@ -999,9 +1187,13 @@ hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lo
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R, s = (int)ms;
   // 16-wave 256 x 256 tiles (each wave 64 x 64: four waves per SIMD hide each other's scale
   // permutes, LDS reads and barrier waits) when they fill the chip, else 4-wave 128 x 128;
-  // W4A4_GEMM_TILE=4x4x2x2, 2x4x4x2 (8 waves of 128 x 64) or 2x2x2x2 forces one
+  // W4A4_GEMM_TILE=4x4x2x2, 2x4x4x2 (8 waves of 128 x 64), 2x2x4x4 (4 waves of 128 x 128 with
+  // register prefetch: half the LDS reads, but measured slower) or 2x2x2x2 forces one
   const char* forced = getenv("W4A4_GEMM_TILE");
   const bool big = forced ? !strcmp(forced, "4x4x2x2") : tile_score(M, N, 256, 256) >= tile_score(M, N, 128, 128);
+  if (forced && !strcmp(forced, "2x2x4x4"))
+    return launch_mx_tile<2, 2, 4, 4, 3, true>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s,
+                                               yp);
   if (forced && !strcmp(forced, "2x4x4x2"))
     return launch_mx_tile<2, 4, 4, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
   if (big) return launch_mx_tile<4, 4, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);

@@ -352,23 +352,11 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
   }
 
   for (int u = u_begin; u < u_end; ++u) {
-    // current unit's raw inputs; prefetch the next unit's
-    u32x4_t xc[US][2];
-#pragma unroll
-    for (int c = 0; c < US; ++c) { xc[c][0] = xr[c][0]; xc[c][1] = xr[c][1]; }
-    uint32_t lac[ACT ? US : 1];
-    u32x4_t lwc[ACT ? 1 : US][2];
-    if constexpr (ACT) {
-#pragma unroll
-      for (int c = 0; c < US; ++c) lac[c] = lar[c];
-    } else {
-#pragma unroll
-      for (int c = 0; c < US; ++c) { lwc[c][0] = lwr[c][0]; lwc[c][1] = lwr[c][1]; }
-    }
-    if (u + 1 < u_end) {
-      load_x(u + 1, xr);
-      if constexpr (ACT) load_lam_act(u + 1, lar); else load_lam_w(u + 1, lwr);
-    }
+    // the current unit's raw inputs (the next unit's are fetched into the same registers once
+    // these are consumed by the smoothing)
+    u32x4_t (&xc)[US][2] = xr;
+    const uint32_t (&lac)[ACT ? US : 1] = lar;
+    const u32x4_t (&lwc)[ACT ? 1 : US][2] = lwr;
     const bool tail = (u + 1) * UC > K;
     if (tail) {  // zero the columns past K (whole blocks, K being a multiple of the block)
 #pragma unroll
@@ -445,6 +433,11 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
             v[c][j] = __uint_as_float(d << 16) * __uint_as_float(l << 16);  // bf16 * bf16: exact
             v[c][j + 1] = __uint_as_float(d & 0xFFFF0000u) * __uint_as_float(l & 0xFFFF0000u);
           }
+    }
+
+    if (u + 1 < u_end) {
+      load_x(u + 1, xr);
+      if constexpr (ACT) load_lam_act(u + 1, lar); else load_lam_w(u + 1, lwr);
     }
 
     if constexpr (LORA) {

@@ -49,5 +49,20 @@ def build(verbose=False, out=None):
     return out
 
 
+def build_probe(verbose=False):
+    """Compile the matrix-core throughput probe (a standalone program, not part of the library)."""
+    out = os.path.join(HERE, "mfma_peak")
+    cmd = [hipcc()] + [f for f in flags() if f not in ("-fPIC", "-shared")] + [
+        os.path.join(HERE, "csrc", "mfma_peak.cpp"), "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

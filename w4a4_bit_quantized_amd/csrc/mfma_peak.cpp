@@ -1,0 +1,134 @@
+// Matrix-core throughput probe for the instructions the GEMMs use (gfx950).
+//
+// Every CU runs one 256-thread workgroup (one wave per SIMD); each wave issues ITER x 8
+// independent matrix instructions into 8 accumulators.  Reported per instruction kind: shader
+// cycles per instruction and wave (s_memtime), wall time (HIP events), the achieved dense
+// TFLOP/s and the implied shader clock.  Operands are either a constant byte pattern or random
+// bits: under random operands the chip draws more power and lowers its clock, which sets the
+// practical ceiling the GEMMs are compared against.  Nothing here is part of the library.
+//
+// Usage: mfma_peak [iterations]   (default 4000)
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+enum Kind { FP4_32x32x64 = 0, FP4_16x16x128 = 1, FP8_32x32x64 = 2, F16_32x32x16 = 3 };
+
+template <int KIND>
+__global__ __launch_bounds__(256) void probe(const int* in, float* out, unsigned long long* cyc, int iters) {
+  const int l = threadIdx.x & 63;
+  const i32x4_t a4 = {in[l], in[l + 1], in[l + 2], in[l + 3]};
+  const i32x8_t a = __builtin_shufflevector(a4, a4, 0, 1, 2, 3, -1, -1, -1, -1);
+  const i32x8_t b = __builtin_shufflevector(a4, a4, 1, 2, 3, 0, -1, -1, -1, -1);
+  const i32x8_t a8 = {in[l], in[l + 1], in[l + 2], in[l + 3], in[l + 4], in[l + 5], in[l + 6], in[l + 7]};
+  half8_t h8;
+  for (int i = 0; i < 8; ++i) h8[i] = (_Float16)(in[l + i] & 7);
+  const int s = 127 | (127 << 8);  // E8M0 scale 1.0 in the bytes the instructions select
+  f32x16_t c[8];
+  f32x4_t d[8];
+  for (int i = 0; i < 8; ++i) {
+    c[i] = f32x16_t{};
+    d[i] = f32x4_t{};
+  }
+  __syncthreads();
+  const unsigned long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (KIND == FP4_32x32x64) c[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[i], 4, 4, 0, s, 0, s);
+      if (KIND == FP4_16x16x128) d[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, d[i], 4, 4, 0, s, 0, s);
+      if (KIND == FP8_32x32x64) c[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, c[i], 0, 0, 0, s, 0, s);
+      if (KIND == F16_32x32x16) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(h8, h8, c[i], 0, 0, 0);
+    }
+  }
+  const unsigned long long t1 = clock64();
+  float acc = 0.f;
+  for (int i = 0; i < 8; ++i) {
+    for (int r = 0; r < 16; ++r) acc += c[i][r];
+    for (int r = 0; r < 4; ++r) acc += d[i][r];
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+  if (threadIdx.x == 0) cyc[blockIdx.x] = t1 - t0;
+}
+
+bool ok(hipError_t e, const char* what) {
+  if (e != hipSuccess) std::fprintf(stderr, "%s: %s\n", what, hipGetErrorString(e));
+  return e == hipSuccess;
+}
+
+template <int KIND>
+bool run(const char* name, const int* in, float* out, unsigned long long* cyc, int blocks, int iters) {
+  hipLaunchKernelGGL(probe<KIND>, dim3(blocks), dim3(256), 0, 0, in, out, cyc, iters);  // warm-up
+  if (!ok(hipDeviceSynchronize(), "warm-up")) return false;
+  hipEvent_t e0, e1;
+  if (!ok(hipEventCreate(&e0), "event") || !ok(hipEventCreate(&e1), "event")) return false;
+  (void)hipEventRecord(e0);
+  hipLaunchKernelGGL(probe<KIND>, dim3(blocks), dim3(256), 0, 0, in, out, cyc, iters);
+  (void)hipEventRecord(e1);
+  if (!ok(hipEventSynchronize(e1), "run")) return false;
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, e0, e1);
+  std::vector<unsigned long long> h(blocks);
+  if (!ok(hipMemcpy(h.data(), cyc, (size_t)blocks * 8, hipMemcpyDeviceToHost), "copy")) return false;
+  double avg = 0;
+  for (auto v : h) avg += (double)v;
+  avg /= blocks;
+  const double n = (double)iters * 8;
+  const double flops = KIND == FP4_16x16x128 ? 2.0 * 16 * 16 * 128 : KIND == F16_32x32x16 ? 2.0 * 32 * 32 * 16
+                                                                                           : 2.0 * 32 * 32 * 64;
+  std::printf("%-26s %5.1f cycles/instr/wave  %7.3f ms  %8.1f TFLOP/s  clock %.2f GHz\n", name, avg / n, ms,
+              flops * n * 4 * blocks / (ms * 1e-3) / 1e12, avg / (ms * 1e-3) / 1e9);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return true;
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  const int iters = argc > 1 ? std::atoi(argv[1]) : 4000;
+  hipDeviceProp_t prop;
+  if (!ok(hipGetDeviceProperties(&prop, 0), "device")) return 1;
+  const int blocks = prop.multiProcessorCount;  // one workgroup (4 waves) per CU
+  int* in = nullptr;
+  float* out = nullptr;
+  unsigned long long* cyc = nullptr;
+  if (!ok(hipMalloc(&in, 1024 * 4), "alloc") || !ok(hipMalloc(&out, (size_t)blocks * 256 * 4), "alloc") ||
+      !ok(hipMalloc(&cyc, (size_t)blocks * 8), "alloc"))
+    return 1;
+  std::vector<int> rnd(1024);
+  unsigned x = 12345u;
+  for (auto& v : rnd) {
+    x = x * 1664525u + 1013904223u;
+    v = (int)(x ^ (x >> 13));
+  }
+  std::printf("%s, %d CUs, %d iterations x 8 instructions per wave\n", prop.gcnArchName, blocks, iters);
+  for (int mode = 0; mode < 2; ++mode) {
+    if (mode == 0) {
+      if (!ok(hipMemset(in, 0x11, 1024 * 4), "memset")) return 1;
+    } else if (!ok(hipMemcpy(in, rnd.data(), 1024 * 4, hipMemcpyHostToDevice), "copy")) {
+      return 1;
+    }
+    std::printf("operands: %s\n", mode == 0 ? "constant bytes 0x11" : "random bits");
+    if (!run<FP4_32x32x64>("fp4 32x32x64 (scaled)", in, out, cyc, blocks, iters) ||
+        !run<FP4_16x16x128>("fp4 16x16x128 (scaled)", in, out, cyc, blocks, iters) ||
+        !run<FP8_32x32x64>("fp8 32x32x64 (scaled)", in, out, cyc, blocks, iters) ||
+        !run<F16_32x32x16>("f16 32x32x16", in, out, cyc, blocks, iters))
+      return 1;
+  }
+  (void)hipFree(in);
+  (void)hipFree(out);
+  (void)hipFree(cyc);
+  return 0;
+}

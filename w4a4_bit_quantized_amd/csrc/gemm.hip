@@ -1186,11 +1186,14 @@ hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lo
   auto yp = static_cast<uint16_t*>(y);
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R, s = (int)ms;
   // 16-wave 256 x 256 tiles (each wave 64 x 64: four waves per SIMD hide each other's scale
-  // permutes, LDS reads and barrier waits) when they fill the chip, else 4-wave 128 x 128;
+  // permutes, LDS reads and barrier waits) unless 4-wave 128 x 128 tiles need fewer rounds of
+  // 256 tiles by more than the measured per-tile time ratio (2.4: 41 vs 17 us at K = 3072);
   // W4A4_GEMM_TILE=4x4x2x2, 2x4x4x2 (8 waves of 128 x 64), 2x2x4x4 (4 waves of 128 x 128 with
   // register prefetch: half the LDS reads, but measured slower) or 2x2x2x2 forces one
   const char* forced = getenv("W4A4_GEMM_TILE");
-  const bool big = forced ? !strcmp(forced, "4x4x2x2") : tile_score(M, N, 256, 256) >= tile_score(M, N, 128, 128);
+  const int64_t rounds256 = ((M + 255) / 256 * ((N + 255) / 256) + 255) / 256;
+  const int64_t rounds128 = ((M + 127) / 128 * ((N + 127) / 128) + 255) / 256;
+  const bool big = forced ? !strcmp(forced, "4x4x2x2") : 2.4 * (double)rounds256 <= (double)rounds128;
   if (forced && !strcmp(forced, "2x2x4x4"))
     return launch_mx_tile<2, 2, 4, 4, 3, true>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s,
                                                yp);

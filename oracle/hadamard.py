@@ -15,13 +15,24 @@ positions (j, j + h), j mod 2h < h, by (a + b, a - b) in float32; after the
 last stage every element is multiplied once by float32(1/sqrt(B)).  This is
 x_block @ H_B^T with H_B the normalised Sylvester matrix.
 
+Standalone transform (section 3.1: the Hadacore kernel, in place or not, also
+applied per head_dim block and to column partitions of a linear layer's output):
+``hadamard_transform`` widens the stored values to float32, applies
+``fwht_blocks`` to the chosen columns of every row, and rounds the result once
+to the storage type (bf16 or f16 to nearest even; float32 unchanged).  Columns
+outside the chosen range are left as they are.
+
 Pins: the pages' worked example [1.2, 0.8, 1.5, 12.0] -> [7.75, -5.05, -5.75,
 5.45]; equality with a dense Sylvester matrix built by the recursion;
 orthogonality H H^T = I and symmetry; involution (applying it twice returns the
-input up to float32 rounding).
+input up to float32 rounding); for the standalone transform, the dense product
+rounded once to the storage type, exact involution for powers of four on small
+integers, and untouched columns outside the partition.
 """
 
 import numpy as np
+
+from . import formats
 
 
 def norm_const(block):
@@ -55,3 +66,44 @@ def fwht_blocks(v, block):
         v = w.reshape(lead + (k,))
         h *= 2
     return (v * norm_const(block)).astype(np.float32)
+
+
+DTYPES = ("bf16", "f16", "f32")
+
+
+def to_f32(stored, dtype):
+    """Stored values (bf16 bit patterns as uint16, float16 or float32 arrays) -> float32 (exact)."""
+    if dtype == "bf16":
+        return formats.bf16_to_f32(np.asarray(stored, dtype=np.uint16))
+    if dtype == "f16":
+        return np.asarray(stored, dtype=np.float16).astype(np.float32)
+    if dtype == "f32":
+        return np.asarray(stored, dtype=np.float32)
+    raise ValueError(dtype)
+
+
+def from_f32(v, dtype):
+    """float32 values -> the storage type, rounded once to nearest even."""
+    v = np.asarray(v, dtype=np.float32)
+    if dtype == "bf16":
+        return formats.bf16_from_f64(v.astype(np.float64))  # float32 -> float64 is exact: one rounding
+    if dtype == "f16":
+        return v.astype(np.float16)  # IEEE round to nearest even
+    if dtype == "f32":
+        return v.copy()
+    raise ValueError(dtype)
+
+
+def hadamard_transform(stored, block, dtype="bf16", start=0, length=None):
+    """Normalised block Sylvester transform of columns [start, start + length) of every row.
+
+    ``stored`` is a 2-D array in the storage type of ``dtype``; returns a new
+    array of the same type where the chosen columns hold the transformed
+    values (rounded once) and every other column is copied unchanged.
+    """
+    stored = np.asarray(stored)
+    out = stored.copy()
+    n = stored.shape[-1] - start if length is None else length
+    v = to_f32(stored[..., start:start + n], dtype)
+    out[..., start:start + n] = from_f32(fwht_blocks(v, block), dtype)
+    return out

@@ -86,3 +86,77 @@ def test_rejects_bad_blocks():
         hadamard.fwht_blocks(np.zeros((1, 48), np.float32), 32)
     with pytest.raises(ValueError):
         hadamard.fwht_blocks(np.zeros((1, 48), np.float32), 24)
+
+
+# ---- the standalone transform (rotate notes, section 3.1: Hadacore, in place, head_dim blocks,
+# output partitions) -------------------------------------------------------------------------
+
+
+def _stored(rng, shape, dtype):
+    x = rng.standard_normal(shape).astype(np.float32) * 3
+    return hadamard.from_f32(x, dtype)
+
+
+@pytest.mark.parametrize("dtype", hadamard.DTYPES)
+@pytest.mark.parametrize("n", [2, 8, 64, 512, 2048])
+def test_standalone_equals_rounded_dense_product(dtype, n):
+    """The transform equals the float64 dense product rounded once to the storage type, except
+    where the float32 butterflies land within a few float32 ulps of a rounding boundary."""
+    rng = np.random.default_rng(n)
+    x = _stored(rng, (3, 2 * n), dtype)
+    got = hadamard.to_f32(hadamard.hadamard_transform(x, n, dtype), dtype).astype(np.float64)
+    h = _sylvester_dense(n) / np.sqrt(n)
+    exact = (hadamard.to_f32(x, dtype).astype(np.float64).reshape(3, 2, n) @ h.T).reshape(3, 2 * n)
+    ref = hadamard.to_f32(hadamard.from_f32(exact.astype(np.float32), dtype), dtype).astype(np.float64)
+    ulp = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -23}[dtype]
+    # float32 butterflies differ from the exact product by about log2(n) float32 ulps of the
+    # block's magnitude; one storage ulp covers the final rounding
+    scale = np.abs(hadamard.to_f32(x, dtype)).reshape(3, 2, n).max(axis=2).repeat(n, axis=1)
+    tol = ulp * np.abs(exact) + (np.log2(n) + 2) * 2.0 ** -23 * np.sqrt(n) * scale
+    assert np.all(np.abs(got - exact) <= tol + 1e-30)
+    if dtype != "f32":  # the storage rounding hides the butterflies' float32 error except near boundaries
+        assert np.mean(got == ref) > 0.95
+
+
+@pytest.mark.parametrize("dtype,n", [("bf16", 4), ("bf16", 16), ("bf16", 64), ("f16", 16), ("f16", 256),
+                                     ("f16", 1024), ("f32", 64), ("f32", 1024), ("f32", 4096)])
+def test_standalone_involution_exact_for_powers_of_four(dtype, n):
+    """Sizes 4^k: 1/sqrt(n) is a power of two, and inputs in {-1, 0, 1} stay exact through both
+    passes while the storage type holds every integer up to n (bf16: n <= 256, f16: n <= 2048)."""
+    rng = np.random.default_rng(3)
+    xi = rng.integers(-1, 2, size=(2, n)).astype(np.float32)
+    x = hadamard.from_f32(xi, dtype)
+    twice = hadamard.hadamard_transform(hadamard.hadamard_transform(x, n, dtype), n, dtype)
+    assert np.array_equal(hadamard.to_f32(twice, dtype), xi)
+
+
+def test_standalone_partition_leaves_other_columns():
+    """An output partition [start, start + length) is transformed; everything else is copied."""
+    rng = np.random.default_rng(5)
+    x = _stored(rng, (4, 96), "bf16")
+    y = hadamard.hadamard_transform(x, 16, "bf16", start=32, length=48)
+    assert np.array_equal(y[:, :32], x[:, :32]) and np.array_equal(y[:, 80:], x[:, 80:])
+    part = hadamard.hadamard_transform(x[:, 32:80], 16, "bf16")
+    assert np.array_equal(y[:, 32:80], part)
+
+
+def test_standalone_head_dim_blocks_equal_separate_rows():
+    """Blocking by head_dim is the transform of each head's slice on its own."""
+    rng = np.random.default_rng(6)
+    x = _stored(rng, (3, 4 * 64), "f16")
+    y = hadamard.hadamard_transform(x, 64, "f16")
+    for h in range(4):
+        assert np.array_equal(y[:, 64 * h:64 * h + 64], hadamard.hadamard_transform(x[:, 64 * h:64 * h + 64], 64, "f16"))
+
+
+def test_storage_rounding_matches_torch():
+    """bf16 and f16 rounding of the float32 result agree with torch's CPU conversions."""
+    import torch
+    rng = np.random.default_rng(8)
+    v = (rng.standard_normal(4096) * np.exp2(rng.integers(-20, 20, 4096))).astype(np.float32)
+    b = hadamard.from_f32(v, "bf16")
+    tb = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b, tb)
+    h = hadamard.from_f32(v, "f16")
+    th = torch.from_numpy(v).to(torch.float16).numpy()
+    assert np.array_equal(h.view(np.uint16), th.view(np.uint16))

@@ -191,6 +191,37 @@ w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscal
                            int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- Standalone block Hadamard transform ------------------------------------------------
+ * Rotate notes, section 3.1 (the Hadacore kernel behind hadacore_transform(x, inplace): the
+ * Sylvester Hadamard transform applied through its recursion, symmetric and therefore its own
+ * inverse, in place or not) and section 3.2 (applied per head_dim block, and to column
+ * partitions [start, start + length) of a layer's output); the Sylvester recursion and the
+ * 1/sqrt(n) normalisation from sections 2.1-2.2.
+ *
+ * For each of `rows` rows and each block of `block` consecutive columns of the first `cols`:
+ *   y[r, blk] = round( float32(1/sqrt(block)) * FWHT(float32(x[r, blk])) )
+ * with butterfly spans 1, 2, ..., block/2 in that order, each pair (a, b) -> (a + b, a - b) in
+ * float32, one multiply, then one round to nearest even into the storage type (bf16 and f16;
+ * f32 is stored as computed).  Results are bit-identical to that sequence of float32
+ * operations (the quantizers' fused rotation uses the same one).
+ *   x, y   device pointers to element (0, 0); row r starts ldx (ldy) elements after row r - 1,
+ *          so a column partition is addressed as x + start with the full row stride.
+ *   ldx, ldy  row strides in elements, >= cols.
+ *   dtype  W4A4_DTYPE_BF16, W4A4_DTYPE_F16 or W4A4_DTYPE_F32 (both tensors).
+ *   block  a power of two in [2, W4A4_HADAMARD_MAX_BLOCK]; cols % block == 0.
+ * x == y (with ldx == ldy) transforms in place; any other overlap of x and y is undefined.
+ * Columns at and past `cols` in each row are not touched.  Errors: W4A4_ERR_SHAPE (negative
+ * sizes, cols % block, ld < cols, x == y with ldx != ldy), W4A4_ERR_UNSUPPORTED (block,
+ * dtype), W4A4_ERR_NULL, W4A4_ERR_ALIGN (x or y not aligned to the element size).  rows == 0
+ * or cols == 0 launches nothing.  16-byte aligned pointers, row strides and column counts that
+ * are multiples of 8 take the vectorised path. */
+#define W4A4_DTYPE_BF16 0
+#define W4A4_DTYPE_F16 1
+#define W4A4_DTYPE_F32 2
+#define W4A4_HADAMARD_MAX_BLOCK 4096
+w4a4_status w4a4_hadamard_transform(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                                    int32_t block, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

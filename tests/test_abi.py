@@ -148,3 +148,22 @@ def test_mx_validation(lib):
     assert g(M=0) == OK
     assert lib.svdq_linear_mx_workspace_bytes(6, 256, 32) == 768 + 256 + 768  # codes, scales (8 x 8 rows), lora
     assert lib.svdq_linear_mx_workspace_bytes(6, 48, 32) == 0
+
+
+# ---- standalone block Hadamard transform --------------------------------------------------------
+
+def test_hadamard_validation(lib):
+    def h(x=P, ldx=64, y=P + 0x1000, ldy=64, rows=4, cols=64, block=16, dtype=0):
+        return lib.w4a4_hadamard_transform(x, ldx, y, ldy, rows, cols, block, dtype, None)
+    assert h(block=3) == ERR_UNSUPPORTED and h(block=1) == ERR_UNSUPPORTED
+    assert h(block=8192, cols=8192, ldx=8192, ldy=8192) == ERR_UNSUPPORTED  # above W4A4_HADAMARD_MAX_BLOCK
+    assert h(dtype=3) == ERR_UNSUPPORTED and h(dtype=-1) == ERR_UNSUPPORTED
+    assert h(cols=72) == ERR_SHAPE                 # cols % block
+    assert h(ldx=32) == ERR_SHAPE and h(ldy=48) == ERR_SHAPE
+    assert h(rows=-1) == ERR_SHAPE and h(cols=-16) == ERR_SHAPE
+    assert h(y=P, ldy=128) == ERR_SHAPE            # in place needs equal row strides
+    assert h(rows=0, x=None, y=None) == OK and h(cols=0, x=None, y=None) == OK
+    assert h(x=None) == ERR_NULL and h(y=None) == ERR_NULL
+    assert h(x=P + 1) == ERR_ALIGN                 # bf16 needs 2-byte alignment
+    assert h(y=P + 2, dtype=2) == ERR_ALIGN        # f32 needs 4-byte alignment
+    assert binding.HADAMARD_MAX_BLOCK == 4096

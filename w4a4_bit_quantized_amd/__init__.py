@@ -12,6 +12,7 @@ __version__ = "0.1.0"
 
 from .binding import (  # noqa: F401
     W4A4Error,
+    hadamard_transform,
     library_path,
     load_library,
     svdq_gemm_lowrank,

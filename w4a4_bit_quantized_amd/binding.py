@@ -38,7 +38,12 @@ SIGNATURES = {
     "svdq_linear_mx_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "svdq_linear_mx": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                       _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "w4a4_hadamard_transform": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p]),
 }
+
+# storage type codes of w4a4_hadamard_transform
+DTYPE_BF16, DTYPE_F16, DTYPE_F32 = 0, 1, 2
+HADAMARD_MAX_BLOCK = 4096
 
 
 class W4A4Error(RuntimeError):
@@ -315,3 +320,49 @@ def svdq_linear_mx(x, layer, hadamard_block=32, workspace=None, out=None):
                             workspace.numel(), _stream(dev))
     _check(st, "svdq_linear_mx")
     return y.reshape(*lead, N)
+
+
+def _rows_view(t, name):
+    """(rows, cols, row stride) of a tensor whose last dimension is dense: 2-D with any row stride
+    (a column partition of a larger matrix), or any shape that flattens to rows without copying."""
+    if t.dim() == 0 or t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a dense last dimension")
+    cols = t.shape[-1]
+    if t.dim() == 1:
+        return 1, cols, cols
+    if t.dim() == 2:
+        if t.shape[0] > 1 and t.stride(0) < cols:
+            raise ValueError(f"{name} rows overlap (row stride {t.stride(0)} < {cols})")
+        return t.shape[0], cols, t.stride(0) if t.shape[0] > 1 else cols
+    if not t.is_contiguous():
+        raise ValueError(f"{name} with more than two dimensions must be contiguous")
+    return t.numel() // max(cols, 1), cols, cols
+
+
+def hadamard_transform(x, block=None, inplace=False, out=None):
+    """Normalised block Sylvester Hadamard transform of the last dimension, per `block` columns
+    (default: the whole last dimension, a power of two up to HADAMARD_MAX_BLOCK); its own inverse.
+
+    x: bf16, f16 or f32 device tensor with a dense last dimension (a 2-D column slice such as
+    y[:, start:start + length] is fine).  inplace=True writes into x and returns it; otherwise
+    the result goes to `out` (same shape and dtype) or a new tensor."""
+    torch = _torch()
+    lib = load_library()
+    codes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16, torch.float32: DTYPE_F32}
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a device tensor")
+    if x.dtype not in codes:
+        raise TypeError(f"x must be bf16, f16 or f32, got {x.dtype}")
+    rows, cols, ldx = _rows_view(x, "x")
+    block = int(cols if block is None else block)
+    if inplace:
+        y = x
+    else:
+        y = torch.empty_like(x, memory_format=torch.contiguous_format) if out is None else out
+        if y.shape != x.shape or y.dtype != x.dtype or y.device != x.device:
+            raise ValueError("out must match x in shape, dtype and device")
+    _, _, ldy = _rows_view(y, "out")
+    st = lib.w4a4_hadamard_transform(_ptr(x), ldx, _ptr(y), ldy, rows, cols, block, codes[x.dtype],
+                                     _stream(x.device))
+    _check(st, "w4a4_hadamard_transform")
+    return y

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
+
 #include "launch.h"
 
 namespace {
@@ -254,6 +256,25 @@ w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscal
   if (st != W4A4_OK) return st;
   return from_hip(w4a4::launch_gemm_mx(qact, ascales, lora, parts, qweight, wscales, proj_up, wcscales, wtscale, M, N,
                                        K, R, mx_rows(M), y, s));
+}
+
+// ---- standalone block Hadamard transform (rotate notes, section 3.1) ------------------------
+
+w4a4_status w4a4_hadamard_transform(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                                    int32_t block, int32_t dtype, void* stream) {
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > (int64_t)1 << 30) return W4A4_ERR_SHAPE;
+  if (block < 2 || block > W4A4_HADAMARD_MAX_BLOCK || (block & (block - 1)) != 0) return W4A4_ERR_UNSUPPORTED;
+  if (dtype < W4A4_DTYPE_BF16 || dtype > W4A4_DTYPE_F32) return W4A4_ERR_UNSUPPORTED;
+  if (cols % block != 0 || ldx < cols || ldy < cols) return W4A4_ERR_SHAPE;
+  if (x == y && ldx != ldy) return W4A4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return W4A4_OK;
+  if (!x || !y) return W4A4_ERR_NULL;
+  const uintptr_t es = dtype == W4A4_DTYPE_F32 ? 4 : 2;
+  if (!aligned(x, es) || !aligned(y, es)) return W4A4_ERR_ALIGN;
+  const float norm = (float)(1.0 / std::sqrt((double)block));
+  (void)hipGetLastError();
+  return from_hip(
+      w4a4::launch_hadamard(x, ldx, y, ldy, rows, cols, block, dtype, norm, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -42,4 +42,10 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
                               const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
                               hipStream_t stream);
 
+// Standalone block Hadamard transform of rows x cols elements (row strides ldx, ldy in
+// elements; dtype 0 bf16, 1 f16, 2 f32; block a power of two in [2, 4096] dividing cols);
+// norm = float32(1 / sqrt(block)).  x == y (with ldx == ldy) transforms in place.
+hipError_t launch_hadamard(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols, int block,
+                           int dtype, float norm, hipStream_t stream);
+
 }  // namespace w4a4

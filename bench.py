@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true", help="also run one 512 MiB device copy (counter calibration)")
     ap.add_argument("--mx", action="store_true",
                     help="the MXFP4 variant (E8M0 scale per 32, group-32 rotation) on the scaled FP4 matrix cores")
+    ap.add_argument("--fwht", action="store_true",
+                    help="the standalone block Hadamard transform, in place, on the workload's activation (M x K bf16)")
+    ap.add_argument("--block", type=int, default=0, help="--fwht block size (default: the workload's, else 128)")
     return ap.parse_args()
 
 
@@ -56,6 +59,7 @@ KERNEL_SOURCES = {
     "gemm": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "gemm_skinny": ["w4a4_bit_quantized_amd/csrc/gemm_skinny.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "gemm_mx": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
+    "hadamard": ["w4a4_bit_quantized_amd/csrc/hadamard.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "quantize": ["w4a4_bit_quantized_amd/csrc/quantize.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
 }
 
@@ -124,12 +128,104 @@ def sleep_cycles(torch, stream, seconds):
     return int(min(seconds / per_cycle, 1 << 31))
 
 
+def cpu_baseline_fwht(M, K, block, seconds):
+    """The oracle's standalone transform (CPU, NumPy) on a bounded row sample of the same tensor shape."""
+    import numpy as np
+    from oracle import hadamard as oh
+    rng = np.random.default_rng(0)
+    rows = 64
+    x = oh.from_f32(rng.standard_normal((rows, K)).astype(np.float32), "bf16")
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oh.hadamard_transform(x, block, "bf16")
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    t = (time.perf_counter() - t0) / reps
+    return {"value": round(2 * rows * K * 2 / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {M} rows of {M} x {K} bf16, blocks of {block}, mean of {reps} runs, {t:.3f} s each "
+                      f"(NumPy, one thread)"}
+
+
+def main_fwht(args):
+    """The standalone block Hadamard transform, in place, over input sets exceeding twice the MALL."""
+    import ctypes
+    import torch
+
+    import w4a4_bit_quantized_amd as w4
+    from w4a4_bit_quantized_amd import binding, synth
+
+    if not os.path.exists(binding.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    lib = w4.load_library()
+    spec = synth.WORKLOADS[args.workload]
+    M, K = spec["M"], spec["K"]
+    block = args.block or spec["B"] or 128
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    per_set = M * K * 2
+    nsets = args.sets or max(1, -(-2 * MALL_BYTES // per_set))
+    g = torch.Generator(device=dev).manual_seed(0)
+    sets = [torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16) for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    fargs = [(ctypes.c_void_p(t.data_ptr()), K, ctypes.c_void_p(t.data_ptr()), K, M, K, block, binding.DTYPE_BF16, sp)
+             for t in sets]
+
+    def step(i):
+        st = lib.w4a4_hadamard_transform(*fargs[i % nsets])
+        if st:
+            raise RuntimeError(f"w4a4_hadamard_transform failed with status {st}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(sleep_cycles(torch, stream, 2e-3 + 20e-6 * args.steps))
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    k_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if args.calib_copy:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+    nbytes = 2 * M * K * 2  # every element read and written once
+    ach = nbytes / (k_us * 1e-6) / 1e9
+    tr = traffic_from_profile("hadamard", args.workload)
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": "hadamard", "traffic": None if tr is None else round(tr)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_fwht(M, K, block, args.cpu_seconds)
+    line = {
+        "metric": "block Hadamard transform GB/s (bf16 read + write) and % of HBM roofline",
+        "value": round(nbytes / (wall_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "storage": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload + "_fwht", "M": M, "K": K, "block": block, "input_sets": nsets},
+        "kernels": {"hadamard": {"avg_us": round(k_us, 3), "algorithmic_bytes": nbytes, "achieved_GBps": round(ach, 1)}},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer's multi-GPU sharding is "
-              f"design-only: see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer's sharding across GPUs "
+              f"is a design, not built here)", file=sys.stderr)
         sys.exit(2)
+    if args.fwht:
+        return main_fwht(args)
 
     import ctypes
     import numpy as np

@@ -15,7 +15,7 @@
 // Work decomposition.  A wave owns a unit of U = max(B, 512) consecutive columns of one row:
 // lane l holds columns 512 g + 8 l .. + 8 of the unit for g < G = U / 512, loaded as 16-byte
 // vectors.  Spans 1, 2, 4 stay inside a lane, spans 8 .. 256 pair lane l with l ^ (span / 8)
-// (ds_bpermute through __shfl_xor), spans of 512 and more pair register groups g and
+// (DPP, ds_swizzle or ds_bpermute: lane_xor), spans of 512 and more pair register groups g and
 // g ^ (span / 512) inside the lane.  A unit past the end of a row leaves its trailing lanes idle
 // (their blocks do not exist: every block lies inside one unit).  Each wave reads its whole unit
 // before writing any of it, so the transform may run in place.
@@ -85,6 +85,21 @@ __device__ __forceinline__ void store8(void* base, int64_t i, const float (&v)[8
   }
 }
 
+// The value of lane l ^ d (d a power of two below 64, known at compile time after unrolling):
+// DPP quad permutes for 1 and 2, ds_swizzle in bit-mask mode (within 32 lanes) for 4, 8 and 16,
+// ds_bpermute for 32.
+__device__ __forceinline__ float lane_xor(float v, int d) {
+  const int b = __float_as_int(v);
+  switch (d) {
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+    case 4: return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (4 << 10)));
+    case 8: return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (8 << 10)));
+    case 16: return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (16 << 10)));
+    default: return __shfl_xor(v, 32);
+  }
+}
+
 // LOG2B = log2(B); VEC: 16-byte vector loads and stores (pointers, row strides and the column
 // count allow them), else one element at a time.
 template <int DT, int LOG2B, bool VEC>
@@ -136,7 +151,7 @@ __global__ __launch_bounds__(64 * FW_WAVES) void fwht_kernel(const void* x, int6
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float p = __shfl_xor(v[g][i], d);
+          const float p = lane_xor(v[g][i], d);
           v[g][i] = upper ? p - v[g][i] : v[g][i] + p;
         }
     }

@@ -10,12 +10,15 @@ What is computed (plain definition, float64, one final rounding to bf16):
     A[m, k]  = e2m1(qact[m, k])    * e4m3(ascales[k // 16, m])
     Wd[n, k] = e2m1(qweight[n, k]) * e4m3(wscales[k // 16, n])
     y[m, n]  = bf16( (A @ Wd^T)[m, n] * wcscales[n] * wtscale
-                     + (lora_act @ proj_up^T)[m, n] )
+                     + (lora_act @ proj_up^T)[m, n] + bias[n] )
 
 Every A and Wd entry has at most 6 significant bits and every product at most
 12, so the dequantized operands and products are exact in float64; the sum is
-the float64 BLAS sum.  Reading where the pages are silent: ``wcscales`` and
-``wtscale`` multiply the quantized product only, not the low-rank term.
+the float64 BLAS sum.  Readings where the pages are silent: ``wcscales`` and
+``wtscale`` multiply the quantized product only, not the low-rank term; the
+optional ``bias (N,)`` (bf16) that the rotate notes' linear wrapper hands to the
+quantized method (section 3.2, ``apply(layer, x, bias)``) is a plain per-output
+offset added before the single rounding, scaled by nothing.
 
 Pins: a pure-Python triple loop over the block-scaled sum
 sum_g sa * sw * sum_{k in g} qa * qw on tiny shapes; the identity-quantizer
@@ -36,7 +39,7 @@ def dequant(packed, scales_t):
     return vals * np.repeat(sd, quant.GROUP, axis=1)
 
 
-def gemm_lowrank(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale):
+def gemm_lowrank(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, bias=None):
     """Quantized product plus epilogue.  Returns (y_bits (M, N) uint16 bf16, y_f64 before rounding)."""
     a = dequant(qact, ascales)
     wd = dequant(qweight, wscales)
@@ -46,6 +49,8 @@ def gemm_lowrank(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, w
     pu = np.asarray(proj_up, dtype=np.float64)
     if pu.shape[1]:
         y = y + np.asarray(lora_act, dtype=np.float64) @ pu.T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
     return formats.bf16_from_f64(y), y
 
 
@@ -53,15 +58,16 @@ def svdq_linear(x, layer, hadamard_block=0):
     """The whole online layer: activation quantization followed by ``gemm_lowrank``.
 
     ``layer`` holds ``qweight, wscales, proj_down, proj_up, smooth_factor,
-    wcscales, wtscale``.  Returns (y_bits, y_f64, (qact, ascales, lora_act)).
+    wcscales, wtscale`` and optionally ``bias``.  Returns (y_bits, y_f64,
+    (qact, ascales, lora_act)).
     """
     qact, ascales, lora = quant.quantize_act(x, layer["smooth_factor"], layer["proj_down"], hadamard_block)
     yb, y = gemm_lowrank(qact, ascales, lora, layer["qweight"], layer["wscales"], layer["proj_up"],
-                         layer["wcscales"], layer["wtscale"])
+                         layer["wcscales"], layer["wtscale"], layer.get("bias"))
     return yb, y, (qact, ascales, lora)
 
 
-def unquantized_reference(x, w, proj_down, proj_up, smooth_factor, wcscales, wtscale):
+def unquantized_reference(x, w, proj_down, proj_up, smooth_factor, wcscales, wtscale, bias=None):
     """Ungated comparison: the same layer with the quantizer replaced by the identity (float64).
 
     x_s R^T (W diag(smooth) R^T)^T = x W^T, so this is
@@ -75,4 +81,6 @@ def unquantized_reference(x, w, proj_down, proj_up, smooth_factor, wcscales, wts
     if pd.shape[1]:
         xs = x64 / np.asarray(smooth_factor, dtype=np.float64)[None, :]
         y = y + (xs @ pd) @ np.asarray(proj_up, dtype=np.float64).T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
     return y

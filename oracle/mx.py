@@ -111,7 +111,7 @@ def dequant_mx(packed, scales_t, rows):
     return vals * np.repeat(sd, MX_GROUP, axis=1)
 
 
-def gemm_lowrank_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale):
+def gemm_lowrank_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, bias=None):
     """MX block-scaled product plus the layer's epilogue.  Returns (y_bits bf16, y_f64)."""
     m, n = qact.shape[0], qweight.shape[0]
     a = dequant_mx(qact, ascales, m)
@@ -122,6 +122,8 @@ def gemm_lowrank_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales
     pu = np.asarray(proj_up, dtype=np.float64)
     if pu.shape[1]:
         y = y + np.asarray(lora_act, dtype=np.float64) @ pu.T
+    if bias is not None:  # the optional per-output offset, as in the nvfp4 layer
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
     return formats.bf16_from_f64(y), y
 
 
@@ -129,5 +131,5 @@ def svdq_linear_mx(x, layer, hadamard_block=32):
     """Whole MX layer: ``quantize_act_mx`` then ``gemm_lowrank_mx``."""
     qact, ascales, lora = quantize_act_mx(x, layer["smooth_factor"], layer["proj_down"], hadamard_block)
     yb, y = gemm_lowrank_mx(qact, ascales, lora, layer["qweight"], layer["wscales"], layer["proj_up"],
-                            layer["wcscales"], layer["wtscale"])
+                            layer["wcscales"], layer["wtscale"], layer.get("bias"))
     return yb, y, (qact, ascales, lora)

@@ -28,7 +28,7 @@ def _e4m3_closed(b):
     return m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
 
 
-def _brute(qact, ascales, lora, qweight, wscales, pu, wcs, wts):
+def _brute(qact, ascales, lora, qweight, wscales, pu, wcs, wts, bias=None):
     M, N, K = qact.shape[0], qweight.shape[0], qact.shape[1] * 2
     R = pu.shape[1]
     y = np.zeros((M, N))
@@ -43,6 +43,8 @@ def _brute(qact, ascales, lora, qweight, wscales, pu, wcs, wts):
                     part += _e2m1_closed(ca) * _e2m1_closed(cw)
                 tot += _e4m3_closed(int(ascales[g, m])) * _e4m3_closed(int(wscales[g, n])) * part
             y[m, n] = tot * float(wcs[n]) * float(wts[0]) + sum(float(lora[m, r]) * float(pu[n, r]) for r in range(R))
+            if bias is not None:
+                y[m, n] += float(bias[n])
     return y
 
 
@@ -55,6 +57,12 @@ def test_gemm_matches_block_scaled_triple_loop(M, K, N, R, B):
     ref = _brute(qa, sa, lora, qw, ws, lay["proj_up"], lay["wcscales"], lay["wtscale"])
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
     assert np.array_equal(yb, formats.bf16_from_f64(ref))
+    # the optional bias: a per-output offset added before the single rounding, scaled by nothing
+    bias = np.float32(np.random.default_rng(M + N).uniform(-3, 3, N))
+    yb2, y2 = linear.gemm_lowrank(qa, sa, lora, qw, ws, lay["proj_up"], lay["wcscales"], lay["wtscale"], bias)
+    ref2 = _brute(qa, sa, lora, qw, ws, lay["proj_up"], lay["wcscales"], lay["wtscale"], bias)
+    assert np.allclose(y2, ref2, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(yb2, formats.bf16_from_f64(ref2))
 
 
 def test_rank_zero_has_no_lowrank_term():

@@ -134,6 +134,9 @@ def test_gemm_mx_matches_triple_loop(M, K, N, R):
     ref = _triple_loop(qa, sa, qw, sw, M, N, K) * wcs[None, :].astype(np.float64)
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
     assert np.array_equal(yb, formats.bf16_from_f64(ref))
+    bias = rng.uniform(-2, 2, N).astype(np.float32)  # the optional per-output offset, unscaled
+    yb2, y2 = mx.gemm_lowrank_mx(qa, sa, lo, qw, sw, pu, wcs, np.float32([1.0]), bias)
+    assert np.allclose(y2, ref + bias.astype(np.float64)[None, :], rtol=1e-12, atol=1e-12)
 
 
 def test_identity_of_rotation_in_the_product():

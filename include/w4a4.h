@@ -191,6 +191,34 @@ w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscal
                            int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- Optional bias -------------------------------------------------------------------------
+ * Rotate notes, section 3.2: the linear-layer wrapper hands the layer's optional bias to the
+ * quantized method (apply(layer, x, bias)).  These four entry points are the ones above with one
+ * more argument, `bias`: bf16 [N] (2-byte aligned) or NULL for none.  It is added in float32 to
+ * each output after the scaled quantized product and the low-rank term, before the single
+ * rounding to bf16, and is not multiplied by wcscales or wtscale:
+ *   y = bf16( acc * wcscales * wtscale + L @ proj_up^T + bias )
+ * Validation and errors are those of the entry point without bias, plus W4A4_ERR_ALIGN for an
+ * odd bias address. */
+w4a4_status svdq_gemm_lowrank_bias(const void* qact, const void* ascales, const float* lora_act,
+                                   const void* qweight, const void* wscales, const void* proj_up,
+                                   const void* wcscales, const void* wtscale, const void* bias, int64_t M,
+                                   int64_t N, int64_t K, int64_t R, void* y, void* stream);
+w4a4_status svdq_linear_bias(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                             const void* proj_up, const void* smooth_factor, const void* wcscales,
+                             const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                             int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
+                             void* stream);
+w4a4_status svdq_gemm_lowrank_mx_bias(const void* qact, const void* ascales, const float* lora_act,
+                                      const void* qweight, const void* wscales, const void* proj_up,
+                                      const void* wcscales, const void* wtscale, const void* bias, int64_t M,
+                                      int64_t N, int64_t K, int64_t R, void* y, void* stream);
+w4a4_status svdq_linear_mx_bias(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                                const void* proj_up, const void* smooth_factor, const void* wcscales,
+                                const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                                int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* ---- Standalone block Hadamard transform ------------------------------------------------
  * Rotate notes, section 3.1 (the Hadacore kernel behind hadacore_transform(x, inplace): the
  * Sylvester Hadamard transform applied through its recursion, symmetric and therefore its own

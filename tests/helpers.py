@@ -80,3 +80,14 @@ def accumulation_bound(qact, ascales, lora, qweight, wscales, proj_up, wcscales,
     if np.asarray(proj_up).shape[1]:
         b = b + np.abs(np.asarray(lora, np.float64)) @ np.abs(np.asarray(proj_up, np.float64)).T
     return n_adds * 2.0 ** -24 * b
+
+
+def seeded_bias(N, seed):
+    """A bf16 bias (N,) in U[-4, 4] (bit patterns), seeded."""
+    from oracle import formats
+    return formats.bf16_from_f64(np.random.default_rng(1000 + seed).uniform(-4.0, 4.0, N))
+
+
+def bf16_values(bits):
+    """bf16 bit patterns -> float32 values (exact)."""
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32)

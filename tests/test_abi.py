@@ -167,3 +167,16 @@ def test_hadamard_validation(lib):
     assert h(x=P + 1) == ERR_ALIGN                 # bf16 needs 2-byte alignment
     assert h(y=P + 2, dtype=2) == ERR_ALIGN        # f32 needs 4-byte alignment
     assert binding.HADAMARD_MAX_BLOCK == 4096
+
+
+def test_bias_validation(lib):
+    g = lambda b, **k: lib.svdq_gemm_lowrank_bias(P, P, P, P, P, P, P, P, b, k.get("M", 16), 64, 256, 32, P, None)
+    assert g(P + 1) == ERR_ALIGN          # bf16 bias needs 2-byte alignment
+    assert g(None, M=0) == OK and g(P + 1, M=0) == OK  # nothing to do: no pointer is looked at
+    gm = lambda b: lib.svdq_gemm_lowrank_mx_bias(P, P, P, P, P, P, P, P, b, 16, 64, 256, 32, P, None)
+    assert gm(P + 1) == ERR_ALIGN
+    lin = lambda b, ws=P: lib.svdq_linear_bias(P, P, P, P, P, P, P, P, b, 16, 64, 256, 32, 0, P, ws, 1 << 20, None)
+    assert lin(P + 3) == ERR_ALIGN
+    assert lin(P, ws=None) == ERR_NULL
+    linm = lambda b: lib.svdq_linear_mx_bias(P, P, P, P, P, P, P, P, b, 16, 64, 256, 32, 32, P, P, 1 << 20, None)
+    assert linm(P + 1) == ERR_ALIGN

@@ -83,24 +83,28 @@ def _accumulation_bound(qa, sa, lo, qw, sw, pu, wcs, wts, M, N, n_adds):
     return n_adds * 2.0 ** -24 * b
 
 
-def _check_gemm_mx(w4, lay):
+def _check_gemm_mx(w4, lay, bias=False):
     import torch
     f = synth.as_f32(lay)
     M, N, K = lay["M"], lay["N"], lay["K"]
     qw, sw = _mx_weights(lay)
     qa, sa, lo = omx.quantize_act_mx(f["x"], f["smooth_factor"], f["proj_down"], lay["B"])
     lo32 = lo.astype(np.float32)
+    b_bits = H.seeded_bias(N, M) if bias else None
     y = w4.svdq_gemm_lowrank_mx(H.to_dev_u8(qa), H.to_dev_u8(sa), torch.from_numpy(lo32).cuda(), H.to_dev_u8(qw),
                                 H.to_dev_u8(sw), H.to_dev_bf16(lay["proj_up"]), H.to_dev_bf16(lay["wcscales"]),
-                                H.to_dev_bf16(lay["wtscale"]))
+                                H.to_dev_bf16(lay["wtscale"]), bias=H.to_dev_bf16(b_bits) if bias else None)
     torch.cuda.synchronize()
-    _, y_ref = omx.gemm_lowrank_mx(qa, sa, lo32, qw, sw, f["proj_up"], f["wcscales"], f["wtscale"])
+    b_f = H.bf16_values(b_bits) if bias else None
+    _, y_ref = omx.gemm_lowrank_mx(qa, sa, lo32, qw, sw, f["proj_up"], f["wcscales"], f["wtscale"], b_f)
     y_gpu = H.from_dev_bf16_f64(y)
     H.assert_gates(y_gpu, y_ref, "gemm_mx")
     bound = _accumulation_bound(qa, sa, lo32, qw, sw, f["proj_up"], f["wcscales"], f["wtscale"], M, N,
                                 n_adds=K // 32 + 4 * lay["R"] + 64)
     err = np.abs(y_gpu - y_ref)
     lim = 2.0 ** -8 * np.abs(y_ref) + bound + 1e-30
+    if bias:  # one more float32 addition
+        lim = lim + 2.0 ** -23 * (np.abs(b_f)[None, :] + np.abs(y_ref))
     assert np.all(err <= lim), f"per-element bound broken: worst excess {np.max(err - lim):.3e}"
 
 
@@ -168,3 +172,28 @@ def test_linear_mx_full_size_dit_mlp_up(w4):
     _, y_ref, _ = omx.svdq_linear_mx(f["x"][rows], sub, 32)
     rel, mx = H.assert_gates(y_gpu, y_ref, "dit_mlp_up mx")
     print(f"\ndit_mlp_up mx: parity rel_fro={rel:.2e} max={mx:.2e}")
+
+
+@pytest.mark.parametrize("tile", ["4x4x2x2", "2x2x4x4", "2x2x2x2"])
+def test_gemm_mx_bias(w4, tile, monkeypatch):
+    """The optional bias (rotate notes, section 3.2) through the MX GEMM's bias entry point."""
+    monkeypatch.setenv("W4A4_GEMM_TILE", tile)
+    _check_gemm_mx(w4, _lay(300, 640, 520, 32, 0, seed=43), bias=True)
+
+
+def test_linear_mx_bias(w4):
+    import torch
+    lay = _lay(64, 512, 264, 32, 32, seed=5)
+    qw, sw = _mx_weights(lay)
+    layer = H.device_layer(lay, qw, sw)
+    b_bits = H.seeded_bias(264, 64)
+    layer["bias"] = H.to_dev_bf16(b_bits)
+    y = w4.svdq_linear_mx(H.to_dev_bf16(lay["x"]).reshape(4, 16, 512), layer, hadamard_block=32)
+    torch.cuda.synchronize()
+    f = synth.as_f32(lay)
+    ref_layer = dict(qweight=qw, wscales=sw, bias=H.bf16_values(b_bits), proj_down=f["proj_down"],
+                     proj_up=f["proj_up"], smooth_factor=f["smooth_factor"], wcscales=f["wcscales"],
+                     wtscale=f["wtscale"])
+    _, y_ref, _ = omx.svdq_linear_mx(f["x"], ref_layer, 32)
+    assert tuple(y.shape) == (4, 16, 264)
+    H.assert_gates(H.from_dev_bf16_f64(y.reshape(64, 264)), y_ref, "svdq_linear_mx with bias")

@@ -93,24 +93,30 @@ def test_quantize_weight_parity(w4, N, K, B):
     assert np.array_equal(ws.cpu().numpy(), s_ref)
 
 
-def _check_gemm(w4, lay, rows=None, cols=None):
-    """GEMM fed with the oracle's quantized tensors; compared with the oracle's float64 result."""
+def _check_gemm(w4, lay, rows=None, cols=None, bias=False):
+    """GEMM fed with the oracle's quantized tensors; compared with the oracle's float64 result.
+    bias=True adds a seeded bf16 bias in U[-4, 4] through the entry point with a bias."""
     import torch
     f = synth.as_f32(lay)
     qw, ws = H.oracle_weights(lay)
     qa, sa, lo = oquant.quantize_act(f["x"], f["smooth_factor"], f["proj_down"], lay["B"])
     lo32 = lo.astype(np.float32)
+    b_bits = H.seeded_bias(lay["N"], lay["M"]) if bias else None
+    b_dev = H.to_dev_bf16(b_bits) if bias else None
     y = w4.svdq_gemm_lowrank(H.to_dev_u8(qa), H.to_dev_u8(sa), torch.from_numpy(lo32).cuda(), H.to_dev_u8(qw),
                              H.to_dev_u8(ws), H.to_dev_bf16(lay["proj_up"]), H.to_dev_bf16(lay["wcscales"]),
-                             H.to_dev_bf16(lay["wtscale"]))
+                             H.to_dev_bf16(lay["wtscale"]), bias=b_dev)
     torch.cuda.synchronize()
-    yb_ref, y_ref = olinear.gemm_lowrank(qa, sa, lo32, qw, ws, f["proj_up"], f["wcscales"], f["wtscale"])
+    b_f = H.bf16_values(b_bits) if bias else None
+    yb_ref, y_ref = olinear.gemm_lowrank(qa, sa, lo32, qw, ws, f["proj_up"], f["wcscales"], f["wtscale"], b_f)
     y_gpu = H.from_dev_bf16_f64(y)
     H.assert_gates(y_gpu, y_ref, "gemm")
     bound = H.accumulation_bound(qa, sa, lo32, qw, ws, f["proj_up"], f["wcscales"], f["wtscale"],
                                  n_adds=lay["K"] // 4 + 4 * lay["R"] + 64)
     err = np.abs(y_gpu - y_ref)
     lim = 2.0 ** -8 * np.abs(y_ref) + bound + 1e-30
+    if bias:  # one more float32 addition
+        lim = lim + 2.0 ** -23 * (np.abs(b_f)[None, :] + np.abs(y_ref))
     assert np.all(err <= lim), f"per-element bound broken: worst excess {np.max(err - lim):.3e}"
     return y_gpu, y_ref
 
@@ -290,3 +296,45 @@ def test_error_status_through_binding(w4):
     with pytest.raises(w4.W4A4Error) as e:
         w4.svdq_linear(H.to_dev_bf16(lay["x"]), H.device_layer(lay, qw, ws), hadamard_block=8)
     assert e.value.status == 4
+
+
+# ---- optional bias (rotate notes, section 3.2: apply(layer, x, bias)) --------------------------
+
+@pytest.mark.parametrize("variant,path,skinny", [(None, None, None), ("2x2x4x4", "dma", None),
+                                                 ("2x2x2x2", "stage", None), (None, None, "wide"),
+                                                 (None, None, "stream"), (None, None, "regs")])
+def test_gemm_bias(w4, variant, path, skinny, monkeypatch):
+    """The bias entry point on every epilogue: the default tile, the fragment-row-wise tile, the
+    register-staged kernel and the three skinny variants."""
+    if variant:
+        monkeypatch.setenv("W4A4_GEMM_TILE", variant)
+    if path:
+        monkeypatch.setenv("W4A4_GEMM_PATH", path)
+    if skinny:
+        monkeypatch.setenv("W4A4_SKINNY_PATH", skinny)
+        lay = synth.make_layer("tiny", seed=17, M=16, K=1024, N=8200 if skinny == "wide" else 520, R=32, B=0,
+                               wcs="uniform")
+    else:
+        lay = synth.make_layer("tiny", seed=19, M=300, K=640, N=520, R=32, B=0, wcs="uniform")
+    _check_gemm(w4, lay, bias=True)
+
+
+@pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 0), (37, 70, 256, 32, 128), (16, 200, 4096, 32, 0)])
+def test_linear_bias_3d_input(w4, M, N, K, R, B):
+    """The whole layer with a bias, on a (2, M/2 or so, K) input: leading dimensions flatten into rows."""
+    import torch
+    lay = synth.make_layer("tiny", seed=23 + M, M=M, K=K, N=N, R=R, B=B, wcs="uniform")
+    qw, ws = H.oracle_weights(lay)
+    layer = H.device_layer(lay, qw, ws)
+    b_bits = H.seeded_bias(N, M)
+    layer["bias"] = H.to_dev_bf16(b_bits)
+    x = H.to_dev_bf16(lay["x"])
+    x3 = x.reshape(1, M, K) if M % 2 else x.reshape(2, M // 2, K)
+    y = w4.svdq_linear(x3, layer, hadamard_block=B)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == tuple(x3.shape[:-1]) + (N,)
+    f = synth.as_f32(lay)
+    ref_layer = dict(qweight=qw, wscales=ws, bias=H.bf16_values(b_bits),
+                     **{k: f[k] for k in ("proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale")})
+    _, y_ref, _ = olinear.svdq_linear(f["x"], ref_layer, B)
+    H.assert_gates(H.from_dev_bf16_f64(y.reshape(M, N)), y_ref, "svdq_linear with bias")

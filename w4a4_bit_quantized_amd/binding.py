@@ -39,6 +39,15 @@ SIGNATURES = {
     "svdq_linear_mx": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                       _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "w4a4_hadamard_transform": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_p]),
+    "svdq_gemm_lowrank_bias": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                              _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "svdq_linear_bias": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                        _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "svdq_gemm_lowrank_mx_bias": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                 _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "svdq_linear_mx_bias": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                           _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t,
+                                           _c_p]),
 }
 
 # storage type codes of w4a4_hadamard_transform
@@ -159,8 +168,8 @@ def svdq_quantize_weight(w, smooth_factor, hadamard_block=0):
     return qweight, wscales
 
 
-def svdq_gemm_lowrank(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, out=None):
-    """Block-scaled FP4 GEMM + epilogue -> y (M, N) bf16."""
+def svdq_gemm_lowrank(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, out=None, bias=None):
+    """Block-scaled FP4 GEMM + epilogue -> y (M, N) bf16; ``bias`` (N,) bf16 is optional."""
     torch = _torch()
     lib = load_library()
     qact = _dev(qact, "qact", _bytes_dtypes())
@@ -177,8 +186,14 @@ def svdq_gemm_lowrank(qact, ascales, lora_act, qweight, wscales, proj_up, wcscal
     R = proj_up.shape[1]
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _dev(y, "y", (torch.bfloat16,), dev)
-    st = lib.svdq_gemm_lowrank(_ptr(qact), _ptr(ascales), _ptr(lora_act), _ptr(qweight), _ptr(wscales),
-                               _ptr(proj_up), _ptr(wcscales), _ptr(wtscale), M, N, K, R, _ptr(y), _stream(dev))
+    if bias is None:
+        st = lib.svdq_gemm_lowrank(_ptr(qact), _ptr(ascales), _ptr(lora_act), _ptr(qweight), _ptr(wscales),
+                                   _ptr(proj_up), _ptr(wcscales), _ptr(wtscale), M, N, K, R, _ptr(y), _stream(dev))
+    else:
+        _dev(bias, "bias", (torch.bfloat16,), dev)
+        st = lib.svdq_gemm_lowrank_bias(_ptr(qact), _ptr(ascales), _ptr(lora_act), _ptr(qweight), _ptr(wscales),
+                                        _ptr(proj_up), _ptr(wcscales), _ptr(wtscale), _ptr(bias), M, N, K, R,
+                                        _ptr(y), _stream(dev))
     _check(st, "svdq_gemm_lowrank")
     return y
 
@@ -190,9 +205,9 @@ def svdq_linear(x, layer, hadamard_block=0, workspace=None, out=None):
     """The whole W4A4 layer.  ``x`` (..., K) bf16; leading dims are flattened into M.
 
     ``layer`` maps the checkpoint names (qweight, wscales, proj_down, proj_up,
-    smooth_factor, wcscales, wtscale) to device tensors.  ``workspace`` (u8,
-    at least svdq_linear_workspace_bytes bytes) and ``out`` may be passed to
-    avoid allocation.
+    smooth_factor, wcscales, wtscale) to device tensors, and optionally ``bias``
+    (N,) bf16.  ``workspace`` (u8, at least svdq_linear_workspace_bytes bytes)
+    and ``out`` may be passed to avoid allocation.
     """
     torch = _torch()
     lib = load_library()
@@ -214,10 +229,15 @@ def svdq_linear(x, layer, hadamard_block=0, workspace=None, out=None):
     _dev(workspace, "workspace", (torch.uint8,), dev)
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _dev(y, "y", (torch.bfloat16,), dev)
-    st = lib.svdq_linear(_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]),
-                         _ptr(t["proj_up"]), _ptr(t["smooth_factor"]), _ptr(t["wcscales"]), _ptr(t["wtscale"]),
-                         M, N, K, R, int(hadamard_block), _ptr(y), _ptr(workspace),
-                         workspace.numel(), _stream(dev))
+    common = (_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]), _ptr(t["proj_up"]),
+              _ptr(t["smooth_factor"]), _ptr(t["wcscales"]), _ptr(t["wtscale"]))
+    tail = (M, N, K, R, int(hadamard_block), _ptr(y), _ptr(workspace), workspace.numel(), _stream(dev))
+    bias = layer.get("bias")
+    if bias is None:
+        st = lib.svdq_linear(*common, *tail)
+    else:
+        _dev(bias, "bias", (torch.bfloat16,), dev)
+        st = lib.svdq_linear_bias(*common, _ptr(bias), *tail)
     _check(st, "svdq_linear")
     return y.reshape(*lead, N)
 
@@ -268,8 +288,9 @@ def svdq_quantize_weight_mx(w, smooth_factor, hadamard_block=32):
     return qweight, wscales
 
 
-def svdq_gemm_lowrank_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, out=None):
-    """MXFP4 GEMM + epilogue -> y (M, N) bf16."""
+def svdq_gemm_lowrank_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, out=None,
+                         bias=None):
+    """MXFP4 GEMM + epilogue -> y (M, N) bf16; ``bias`` (N,) bf16 is optional."""
     torch = _torch()
     lib = load_library()
     qact = _dev(qact, "qact", _bytes_dtypes())
@@ -286,14 +307,20 @@ def svdq_gemm_lowrank_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcs
     R = proj_up.shape[1]
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _dev(y, "y", (torch.bfloat16,), dev)
-    st = lib.svdq_gemm_lowrank_mx(_ptr(qact), _ptr(ascales), _ptr(lora_act), _ptr(qweight), _ptr(wscales),
-                                  _ptr(proj_up), _ptr(wcscales), _ptr(wtscale), M, N, K, R, _ptr(y), _stream(dev))
+    if bias is None:
+        st = lib.svdq_gemm_lowrank_mx(_ptr(qact), _ptr(ascales), _ptr(lora_act), _ptr(qweight), _ptr(wscales),
+                                      _ptr(proj_up), _ptr(wcscales), _ptr(wtscale), M, N, K, R, _ptr(y), _stream(dev))
+    else:
+        _dev(bias, "bias", (torch.bfloat16,), dev)
+        st = lib.svdq_gemm_lowrank_mx_bias(_ptr(qact), _ptr(ascales), _ptr(lora_act), _ptr(qweight), _ptr(wscales),
+                                           _ptr(proj_up), _ptr(wcscales), _ptr(wtscale), _ptr(bias), M, N, K, R,
+                                           _ptr(y), _stream(dev))
     _check(st, "svdq_gemm_lowrank_mx")
     return y
 
 
 def svdq_linear_mx(x, layer, hadamard_block=32, workspace=None, out=None):
-    """The whole MXFP4 layer (``layer`` as for ``svdq_linear``, with MX qweight / wscales)."""
+    """The whole MXFP4 layer (``layer`` as for ``svdq_linear``, with MX qweight / wscales; optional ``bias``)."""
     torch = _torch()
     lib = load_library()
     lead = x.shape[:-1]
@@ -314,10 +341,15 @@ def svdq_linear_mx(x, layer, hadamard_block=32, workspace=None, out=None):
     _dev(workspace, "workspace", (torch.uint8,), dev)
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _dev(y, "y", (torch.bfloat16,), dev)
-    st = lib.svdq_linear_mx(_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]),
-                            _ptr(t["proj_up"]), _ptr(t["smooth_factor"]), _ptr(t["wcscales"]), _ptr(t["wtscale"]),
-                            M, N, K, R, int(hadamard_block), _ptr(y), _ptr(workspace),
-                            workspace.numel(), _stream(dev))
+    common = (_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]), _ptr(t["proj_up"]),
+              _ptr(t["smooth_factor"]), _ptr(t["wcscales"]), _ptr(t["wtscale"]))
+    tail = (M, N, K, R, int(hadamard_block), _ptr(y), _ptr(workspace), workspace.numel(), _stream(dev))
+    bias = layer.get("bias")
+    if bias is None:
+        st = lib.svdq_linear_mx(*common, *tail)
+    else:
+        _dev(bias, "bias", (torch.bfloat16,), dev)
+        st = lib.svdq_linear_mx_bias(*common, _ptr(bias), *tail)
     _check(st, "svdq_linear_mx")
     return y.reshape(*lead, N)
 

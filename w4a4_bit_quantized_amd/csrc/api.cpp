@@ -99,14 +99,23 @@ w4a4_status svdq_quantize_weight(const void* w, const void* smooth_factor, int64
                                         wscales, nullptr, static_cast<hipStream_t>(stream)));
 }
 
+w4a4_status svdq_gemm_lowrank_bias(const void* qact, const void* ascales, const float* lora_act, const void* qweight,
+                                   const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
+                                   const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
+                                   void* stream) {
+  w4a4_status st = validate_gemm(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if (bias && !aligned(bias, 2)) return W4A4_ERR_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(w4a4::launch_gemm(qact, ascales, lora_act, 1, qweight, wscales, proj_up, wcscales, wtscale, bias, M,
+                                    N, K, R, y, static_cast<hipStream_t>(stream)));
+}
+
 w4a4_status svdq_gemm_lowrank(const void* qact, const void* ascales, const float* lora_act, const void* qweight,
                               const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
                               int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream) {
-  w4a4_status st = validate_gemm(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
-  if (st != W4A4_OK || M == 0 || N == 0) return st;
-  (void)hipGetLastError();
-  return from_hip(w4a4::launch_gemm(qact, ascales, lora_act, 1, qweight, wscales, proj_up, wcscales, wtscale, M, N,
-                                    K, R, y, static_cast<hipStream_t>(stream)));
+  return svdq_gemm_lowrank_bias(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, nullptr, M, N,
+                                K, R, y, stream);
 }
 
 size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int64_t R) {
@@ -116,10 +125,10 @@ size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int64_t R) {
   return align256(m * k / 2) + align256(k / 16 * m) + align256(parts * m * r * sizeof(float));
 }
 
-w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales, const void* proj_down,
-                        const void* proj_up, const void* smooth_factor, const void* wcscales, const void* wtscale,
-                        int64_t M, int64_t N, int64_t K, int64_t R, int32_t hadamard_block, void* y, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+w4a4_status svdq_linear_bias(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                             const void* proj_up, const void* smooth_factor, const void* wcscales,
+                             const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                             int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes, void* stream) {
   w4a4_status st = check_k_rank_block(K, R, hadamard_block);
   if (st != W4A4_OK) return st;
   if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return W4A4_ERR_SHAPE;
@@ -129,7 +138,7 @@ w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales,
   if (!workspace) return W4A4_ERR_NULL;
   const size_t need = svdq_linear_workspace_bytes(M, K, R);
   if (workspace_bytes < need) return W4A4_ERR_SHAPE;
-  if (!aligned(workspace, 256)) return W4A4_ERR_ALIGN;
+  if (!aligned(workspace, 256) || (bias && !aligned(bias, 2))) return W4A4_ERR_ALIGN;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   void* qact = ws;
   void* ascales = ws + align256((size_t)M * K / 2);
@@ -145,8 +154,16 @@ w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales,
   st = from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, parts, qact, ascales,
                                       lora, s));
   if (st != W4A4_OK) return st;
-  return from_hip(w4a4::launch_gemm(qact, ascales, lora, parts, qweight, wscales, proj_up, wcscales, wtscale, M, N, K,
-                                    R, y, s));
+  return from_hip(w4a4::launch_gemm(qact, ascales, lora, parts, qweight, wscales, proj_up, wcscales, wtscale, bias, M,
+                                    N, K, R, y, s));
+}
+
+w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                        const void* proj_up, const void* smooth_factor, const void* wcscales, const void* wtscale,
+                        int64_t M, int64_t N, int64_t K, int64_t R, int32_t hadamard_block, void* y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return svdq_linear_bias(x, qweight, wscales, proj_down, proj_up, smooth_factor, wcscales, wtscale, nullptr, M, N, K,
+                          R, hadamard_block, y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -206,15 +223,24 @@ w4a4_status svdq_quantize_weight_mx(const void* w, const void* smooth_factor, in
                                         wscales, nullptr, static_cast<hipStream_t>(stream), true, N));
 }
 
-w4a4_status svdq_gemm_lowrank_mx(const void* qact, const void* ascales, const float* lora_act, const void* qweight,
-                                 const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
-                                 int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream) {
+w4a4_status svdq_gemm_lowrank_mx_bias(const void* qact, const void* ascales, const float* lora_act,
+                                      const void* qweight, const void* wscales, const void* proj_up,
+                                      const void* wcscales, const void* wtscale, const void* bias, int64_t M,
+                                      int64_t N, int64_t K, int64_t R, void* y, void* stream) {
   w4a4_status st =
       validate_gemm_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
   if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if (bias && !aligned(bias, 2)) return W4A4_ERR_ALIGN;
   (void)hipGetLastError();
-  return from_hip(w4a4::launch_gemm_mx(qact, ascales, lora_act, 1, qweight, wscales, proj_up, wcscales, wtscale, M,
-                                       N, K, R, mx_rows(M), y, static_cast<hipStream_t>(stream)));
+  return from_hip(w4a4::launch_gemm_mx(qact, ascales, lora_act, 1, qweight, wscales, proj_up, wcscales, wtscale, bias,
+                                       M, N, K, R, mx_rows(M), y, static_cast<hipStream_t>(stream)));
+}
+
+w4a4_status svdq_gemm_lowrank_mx(const void* qact, const void* ascales, const float* lora_act, const void* qweight,
+                                 const void* wscales, const void* proj_up, const void* wcscales, const void* wtscale,
+                                 int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream) {
+  return svdq_gemm_lowrank_mx_bias(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, nullptr, M,
+                                   N, K, R, y, stream);
 }
 
 size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int64_t R) {
@@ -224,10 +250,11 @@ size_t svdq_linear_mx_workspace_bytes(int64_t M, int64_t K, int64_t R) {
   return align256(m * k / 2) + align256(k / 32 * (size_t)mx_rows(M)) + align256(parts * m * r * sizeof(float));
 }
 
-w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscales, const void* proj_down,
-                           const void* proj_up, const void* smooth_factor, const void* wcscales, const void* wtscale,
-                           int64_t M, int64_t N, int64_t K, int64_t R, int32_t hadamard_block, void* y,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+w4a4_status svdq_linear_mx_bias(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                                const void* proj_up, const void* smooth_factor, const void* wcscales,
+                                const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                                int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   w4a4_status st = check_mx(K, R, hadamard_block, true);
   if (st != W4A4_OK) return st;
   if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || N % 4 != 0) return W4A4_ERR_SHAPE;
@@ -237,7 +264,7 @@ w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscal
   if (!workspace) return W4A4_ERR_NULL;
   const size_t need = svdq_linear_mx_workspace_bytes(M, K, R);
   if (workspace_bytes < need) return W4A4_ERR_SHAPE;
-  if (!aligned(workspace, 256)) return W4A4_ERR_ALIGN;
+  if (!aligned(workspace, 256) || (bias && !aligned(bias, 2))) return W4A4_ERR_ALIGN;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   void* qact = ws;
   void* ascales = ws + align256((size_t)M * K / 2);
@@ -254,8 +281,16 @@ w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscal
   st = from_hip(w4a4::launch_quantize(true, x, smooth_factor, proj_down, M, K, R, hadamard_block, parts, qact, ascales,
                                       lora, s, true, mx_rows(M)));
   if (st != W4A4_OK) return st;
-  return from_hip(w4a4::launch_gemm_mx(qact, ascales, lora, parts, qweight, wscales, proj_up, wcscales, wtscale, M, N,
-                                       K, R, mx_rows(M), y, s));
+  return from_hip(w4a4::launch_gemm_mx(qact, ascales, lora, parts, qweight, wscales, proj_up, wcscales, wtscale, bias,
+                                       M, N, K, R, mx_rows(M), y, s));
+}
+
+w4a4_status svdq_linear_mx(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                           const void* proj_up, const void* smooth_factor, const void* wcscales, const void* wtscale,
+                           int64_t M, int64_t N, int64_t K, int64_t R, int32_t hadamard_block, void* y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return svdq_linear_mx_bias(x, qweight, wscales, proj_down, proj_up, smooth_factor, wcscales, wtscale, nullptr, M, N,
+                             K, R, hadamard_block, y, workspace, workspace_bytes, stream);
 }
 
 // ---- standalone block Hadamard transform (rotate notes, section 3.1) ------------------------

@@ -76,8 +76,8 @@ struct Tile {
   static constexpr int SCALE_BYTES = 8 * ROWS * 2;  // f16 scales laid out [group][row]
   static constexpr int STAGE_BYTES = ROWS * CODE_STRIDE + SCALE_BYTES;
   // Epilogue operands, staged in the stage buffers after the K loop: L hi and lo parts
-  // [BM][64] bf16, proj_up [BN][64] bf16 and the column scale [BN] f32.
-  static constexpr int EPI_BYTES = BM * 64 * 2 * 2 + BN * 64 * 2 + BN * 4;
+  // [BM][64] bf16, proj_up [BN][64] bf16, the column scale [BN] f32 and the bias [BN] f32.
+  static constexpr int EPI_BYTES = BM * 64 * 2 * 2 + BN * 64 * 2 + BN * 8;
   // Waves with 16 or more accumulator fragments (which fill the accumulation registers) finish
   // one fragment row at a time, each wave through a 32-row store region of its own placed after
   // the epilogue operands.
@@ -86,7 +86,8 @@ struct Tile {
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_LDS ? 2 * STAGE_BYTES : EPI_LDS;
 };
 
-// Stage a tile's epilogue operands in LDS: the column scales wcscales * wtscale, and for the
+// Stage a tile's epilogue operands in LDS: the column scales wcscales * wtscale, the bias (zero
+// without one), and for the
 // ranks [0, rp) the low-rank activations summed over their `parts` partial sums (in order) and
 // split into bf16 hi + lo parts, and proj_up.  Padded ranks and rows past M or N are zero or
 // clamped.  Each thread issues all its loads of a 16-rank block before storing any of them.
@@ -94,15 +95,17 @@ template <class T, bool LORA>
 __device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int rp, int t, int m0, int n0, int M, int N,
                                                int R, int parts, const float* __restrict__ lora,
                                                const uint16_t* __restrict__ pu, const uint16_t* __restrict__ wcs,
-                                               const uint16_t* __restrict__ wts) {
+                                               const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias) {
   uint16_t* l_hi = reinterpret_cast<uint16_t*>(base);
   uint16_t* l_lo = l_hi + T::BM * rs;
   uint16_t* p_lds = l_lo + T::BM * rs;
   float* c_lds = reinterpret_cast<float*>(p_lds + T::BN * rs);
+  float* b_lds = c_lds + T::BN;
   const float ts = bf16_bits_to_f32(wts[0]);
   for (int c = t; c < T::BN; c += T::THREADS) {
     const int n = n0 + c;
     c_lds[c] = n < N ? bf16_bits_to_f32(wcs[n]) * ts : 0.0f;
+    b_lds[c] = (bias != nullptr && n < N) ? bf16_bits_to_f32(bias[n]) : 0.0f;
   }
   if (!LORA) return;
   constexpr int LI = (T::BM * 16 + T::THREADS - 1) / T::THREADS;
@@ -341,20 +344,23 @@ template <class T, bool LORA>
 __device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N], uint8_t* lds, int t, int m0,
                                          int n0, int M, int N, int R, int parts, const float* __restrict__ lora,
                                          const uint16_t* __restrict__ pu, const uint16_t* __restrict__ wcs,
-                                         const uint16_t* __restrict__ wts, uint16_t* __restrict__ y) {
+                                         const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias,
+                                         uint16_t* __restrict__ y) {
   constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
   constexpr int rs = 64;  // rank stride of the staged operands (compiled maximum rank)
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int l32 = lane & 31, h = lane >> 5;
   const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank
-  stage_epilogue<T, LORA>(lds, rs, rp, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts);
+  stage_epilogue<T, LORA>(lds, rs, rp, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
   __syncthreads();
   const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
   const uint16_t* l_hi = reinterpret_cast<const uint16_t*>(lds);
   const uint16_t* l_lo = l_hi + T::BM * rs;
   const uint16_t* p_lds = l_lo + T::BM * rs;
   const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
+  const float* b_lds = c_lds + T::BN;
+  const bool has_bias = bias != nullptr;
   if constexpr (T::ROWWISE) {
     // Same arithmetic, in the same order per element, one fragment at a time; each fragment
     // row then leaves through the wave's store region (16-byte stores) or, when y rows are not
@@ -384,6 +390,14 @@ __device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N],
             const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
             a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv, lhi, a, 0, 0, 0);
             a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv, llo, a, 0, 0, 0);
+          }
+        }
+        if (has_bias) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4_t b = *reinterpret_cast<const float4_t*>(b_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[4 * q + e] += b[e];
           }
         }
 #pragma unroll
@@ -449,6 +463,18 @@ __device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N],
         }
       }
     }
+  }
+  if (has_bias) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4_t b = *reinterpret_cast<const float4_t*>(b_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] += b[e];
+      }
   }
   if ((N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
     // Coalesced stores: each wave passes its rounded tile through a private LDS region (IC fragment
@@ -520,7 +546,7 @@ template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16, bool LORA, bool 
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
-    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R,
     uint16_t* __restrict__ y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
@@ -597,7 +623,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   }
 
   // the K loop ended with a barrier: the stage buffers are free for the epilogue operands
-  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
+  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, y);
 }
 
 // ---- three-stage variant with direct global -> LDS loads -----------------------------
@@ -664,7 +690,7 @@ template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
-    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R,
     uint16_t* __restrict__ y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
   using D = DmaTile<T>;
@@ -767,7 +793,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
   }
   vm_wait_barrier<0>();  // the last reloads land before the epilogue reuses LDS
 
-  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
+  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, y);
 }
 
 // ---- MXFP4 variant (rotate notes, section 3.3: FP-Quant mxfp4, matmul_mxf4_bf16) ----------
@@ -924,7 +950,7 @@ template <int WAVES_M, int WAVES_N, int FM, int FN, int S, bool PF, bool LORA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
-    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R, int ms,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R, int ms,
     uint16_t* __restrict__ y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
   using D = DmaTileMx<T, S>;
@@ -1009,7 +1035,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
       mx_pf_step<T, D, S>(kt, sl, nkt, lds, acc, wave, wm, wn, l32, h, psel, c_base, c_off, s_base, s_off, s_stride,
                           sA0, sB0, cA0, cB0, sA1, sB1, cA1, cB1);
     vm_wait_barrier<0>();
-    epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
+    epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, y);
     return;
   }
 
@@ -1036,34 +1062,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
   }
   vm_wait_barrier<0>();
 
-  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, y);
+  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, y);
 }
 
 template <int WAVES_M, int WAVES_N, int FM, int FN, int S = 3, bool PF = false>
 hipError_t launch_mx_tile(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                           const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
-                          const uint16_t* wts, int M, int N, int K, int R, int ms, uint16_t* y) {
+                          const uint16_t* wts, const uint16_t* bias, int M, int N, int K, int R, int ms, uint16_t* y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
   dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
   dim3 block(T::THREADS);
   if (rb > 0)
-    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, PF, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
+    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, PF, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, ms, y);
   else
-    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, PF, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, ms, y);
+    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, PF, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, ms, y);
   return hipGetLastError();
 }
 
 template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16>
 hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                      const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
-                     const uint16_t* wts, int M, int N, int K, int R, uint16_t* y) {
+                     const uint16_t* wts, const uint16_t* bias, int M, int N, int K, int R, uint16_t* y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
   dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
   dim3 block(T::THREADS);
   const bool sc4 = (M % 4) == 0 && (N % 4) == 0 &&
                    ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sw)) & 3) == 0;
 #define W4A4_GEMM_GO(L, S) \
-  gemm_kernel<WAVES_M, WAVES_N, FM, FN, VEC16, L, S><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y)
+  gemm_kernel<WAVES_M, WAVES_N, FM, FN, VEC16, L, S><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y)
   if (rb > 0) {
     if (sc4) W4A4_GEMM_GO(true, true); else W4A4_GEMM_GO(true, false);
   } else {
@@ -1076,25 +1102,25 @@ hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* s
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 hipError_t launch_dma(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                       const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
-                      const uint16_t* wts, int M, int N, int K, int R, uint16_t* y) {
+                      const uint16_t* wts, const uint16_t* bias, int M, int N, int K, int R, uint16_t* y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
   dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
   dim3 block(T::THREADS);
   if (rb > 0)
-    gemm_dma_kernel<WAVES_M, WAVES_N, FM, FN, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+    gemm_dma_kernel<WAVES_M, WAVES_N, FM, FN, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
   else
-    gemm_dma_kernel<WAVES_M, WAVES_N, FM, FN, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+    gemm_dma_kernel<WAVES_M, WAVES_N, FM, FN, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
   return hipGetLastError();
 }
 
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 hipError_t launch_tile(bool dma, int rb, bool vec16, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora,
                        int parts, const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
-                       const uint16_t* wts, int M, int N, int K, int R, uint16_t* y) {
-  if (dma) return launch_dma<WAVES_M, WAVES_N, FM, FN>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+                       const uint16_t* wts, const uint16_t* bias, int M, int N, int K, int R, uint16_t* y) {
+  if (dma) return launch_dma<WAVES_M, WAVES_N, FM, FN>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
   if (vec16)
-    return launch_rb<WAVES_M, WAVES_N, FM, FN, true>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
-  return launch_rb<WAVES_M, WAVES_N, FM, FN, false>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+    return launch_rb<WAVES_M, WAVES_N, FM, FN, true>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
+  return launch_rb<WAVES_M, WAVES_N, FM, FN, false>(rb, st, qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
 }
 
 // Score of a tile shape for an M x N problem: fill of whole waves of 256 CUs times the useful
@@ -1120,10 +1146,11 @@ constexpr Variant kVariants[] = {
 
 hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora, int lora_parts,
                        const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
-                       const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, void* y, hipStream_t stream) {
+                       const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
+                       hipStream_t stream) {
   if (M <= SKINNY_MAX_M && !getenv("W4A4_GEMM_TILE"))
-    return launch_gemm_skinny(qact, ascales, lora, lora_parts, qweight, wscales, proj_up, wcscales, wtscale, M, N, K,
-                              R, y, stream);
+    return launch_gemm_skinny(qact, ascales, lora, lora_parts, qweight, wscales, proj_up, wcscales, wtscale, bias, M, N,
+                              K, R, y, stream);
   const int rb = (int)((R + 15) / 16);
   const bool vec16 = (K % 32) == 0;
   auto qa = static_cast<const uint8_t*>(qact);
@@ -1133,6 +1160,7 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
   auto pu = static_cast<const uint16_t*>(proj_up);
   auto wc = static_cast<const uint16_t*>(wcscales);
   auto wt = static_cast<const uint16_t*>(wtscale);
+  auto bs = static_cast<const uint16_t*>(bias);
   auto yp = static_cast<uint16_t*>(y);
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R;
   // The three-stage kernel with direct LDS loads needs whole 128-column K-steps and dword-aligned
@@ -1157,7 +1185,7 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
     for (int i = 0; i < (int)(sizeof(kVariants) / sizeof(kVariants[0])); ++i)
       if (!strcmp(forced, kVariants[i].name)) best = i;
 #define W4A4_TILE_CASE(I, WM, WN, FM, FN) \
-  case I: return launch_tile<WM, WN, FM, FN>(dma, rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+  case I: return launch_tile<WM, WN, FM, FN>(dma, rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
   switch (best) {
     W4A4_TILE_CASE(0, 2, 2, 4, 4)
     W4A4_TILE_CASE(1, 2, 2, 4, 3)
@@ -1166,15 +1194,15 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
     W4A4_TILE_CASE(4, 4, 2, 2, 4)
     W4A4_TILE_CASE(5, 2, 4, 4, 2)
     default:
-      return launch_tile<4, 2, 2, 3>(dma, rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+      return launch_tile<4, 2, 2, 3>(dma, rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
   }
 #undef W4A4_TILE_CASE
 }
 
 hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lora, int lora_parts,
                           const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
-                          const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, int64_t ms, void* y,
-                          hipStream_t stream) {
+                          const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                          int64_t ms, void* y, hipStream_t stream) {
   const int rb = (int)((R + 15) / 16);
   auto qa = static_cast<const uint8_t*>(qact);
   auto sa = static_cast<const uint8_t*>(ascales);
@@ -1183,6 +1211,7 @@ hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lo
   auto pu = static_cast<const uint16_t*>(proj_up);
   auto wc = static_cast<const uint16_t*>(wcscales);
   auto wt = static_cast<const uint16_t*>(wtscale);
+  auto bs = static_cast<const uint16_t*>(bias);
   auto yp = static_cast<uint16_t*>(y);
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R, s = (int)ms;
   // 16-wave 256 x 256 tiles (each wave 64 x 64: four waves per SIMD hide each other's scale
@@ -1195,12 +1224,12 @@ hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lo
   const int64_t rounds128 = ((M + 127) / 128 * ((N + 127) / 128) + 255) / 256;
   const bool big = forced ? !strcmp(forced, "4x4x2x2") : 2.4 * (double)rounds256 <= (double)rounds128;
   if (forced && !strcmp(forced, "2x2x4x4"))
-    return launch_mx_tile<2, 2, 4, 4, 3, true>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s,
+    return launch_mx_tile<2, 2, 4, 4, 3, true>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s,
                                                yp);
   if (forced && !strcmp(forced, "2x4x4x2"))
-    return launch_mx_tile<2, 4, 4, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
-  if (big) return launch_mx_tile<4, 4, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
-  return launch_mx_tile<2, 2, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, s, yp);
+    return launch_mx_tile<2, 4, 4, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s, yp);
+  if (big) return launch_mx_tile<4, 4, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s, yp);
+  return launch_mx_tile<2, 2, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s, yp);
 }
 
 }  // namespace w4a4

@@ -109,7 +109,7 @@ template <int MB, bool VEC16, bool LORA>
 __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
-    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R,
     uint16_t* __restrict__ y) {
   constexpr int MR = 16 * MB;  // padded rows
   __shared__ float red[SK_WAVES][MR][SK_BN];
@@ -208,6 +208,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(
       for (int r = 0; r < R; ++r) l = __builtin_fmaf(l_lds[m * W4A4_MAX_RANK + r], p_lds[n * (W4A4_MAX_RANK + 1) + r], l);
       v += l;
     }
+    if (bias != nullptr) v += bf16_bits_to_f32(bias[gn]);
     y[(size_t)m * N + gn] = (uint16_t)f32_to_bf16_bits(v);
   }
 }
@@ -238,7 +239,7 @@ template <bool LORA>
 __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_stream_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
-    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R,
     uint16_t* __restrict__ y) {
   constexpr int MR = 16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SS_LDS];
@@ -381,6 +382,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_stream_kernel(
       for (int r = 0; r < R; ++r) l = __builtin_fmaf(l_lds[mm * W4A4_MAX_RANK + r], p_lds[n * (W4A4_MAX_RANK + 1) + r], l);
       v += l;
     }
+    if (bias != nullptr) v += bf16_bits_to_f32(bias[gn]);
     y[(size_t)mm * N + gn] = (uint16_t)f32_to_bf16_bits(v);
   }
 }
@@ -440,7 +442,7 @@ template <bool LORA, int RP, bool FULL>
 __global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_wide_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
     const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
-    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, int M, int N, int K, int R,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R,
     uint16_t* __restrict__ y) {
   static_assert(!LORA || RP == 32 || RP == 64, "rank padded to one or two MFMA steps");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SW_LDS];
@@ -581,18 +583,19 @@ __global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_wide_kernel(
   for (int w = 0; w < SW_WAVES; ++w) s += red[(w * 16 + m) * SW_RED + n];
   float v = s * c_lds[n];
   if (LORA) v += red[(SW_WAVES * 16 + m) * SW_RED + n];
+  if (bias != nullptr) v += bf16_bits_to_f32(bias[min(n0 + n, N - 1)]);
   if (m < M && n0 + n < N) y[(size_t)m * N + n0 + n] = (uint16_t)f32_to_bf16_bits(v);
 }
 
 template <int MB, bool VEC16>
 hipError_t launch_mb(bool lora_on, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                      const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs, const uint16_t* wts,
-                     int M, int N, int K, int R, uint16_t* y) {
+                     const uint16_t* bias, int M, int N, int K, int R, uint16_t* y) {
   dim3 grid((unsigned)((N + SK_BN - 1) / SK_BN)), block(64 * SK_WAVES);
   if (lora_on)
-    gemm_skinny_kernel<MB, VEC16, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+    gemm_skinny_kernel<MB, VEC16, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
   else
-    gemm_skinny_kernel<MB, VEC16, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, M, N, K, R, y);
+    gemm_skinny_kernel<MB, VEC16, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
   return hipGetLastError();
 }
 
@@ -600,8 +603,8 @@ hipError_t launch_mb(bool lora_on, hipStream_t st, const uint8_t* qa, const uint
 
 hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float* lora, int lora_parts,
                               const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
-                              const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
-                              hipStream_t stream) {
+                              const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                              void* y, hipStream_t stream) {
   auto qa = static_cast<const uint8_t*>(qact);
   auto sa = static_cast<const uint8_t*>(ascales);
   auto qw = static_cast<const uint8_t*>(qweight);
@@ -609,6 +612,7 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
   auto pu = static_cast<const uint16_t*>(proj_up);
   auto wc = static_cast<const uint16_t*>(wcscales);
   auto wt = static_cast<const uint16_t*>(wtscale);
+  auto bs = static_cast<const uint16_t*>(bias);
   auto yp = static_cast<uint16_t*>(y);
   const bool vec16 = (K % 32) == 0, lo = R > 0;
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R;
@@ -627,7 +631,7 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
     dim3 grid((unsigned)((N + SW_BN - 1) / SW_BN)), block(64 * SW_WAVES);
     const bool full = K == 2 * SS_CH * SS_MAXC;
 #define W4A4_SW_LAUNCH(LO, RP, FU) \
-  gemm_skinny_wide_kernel<LO, RP, FU><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp)
+  gemm_skinny_wide_kernel<LO, RP, FU><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp)
     if (!lo) {
       if (full) W4A4_SW_LAUNCH(false, 0, true); else W4A4_SW_LAUNCH(false, 0, false);
     } else if (r <= 32) {
@@ -641,17 +645,17 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
   if (streamed) {
     dim3 grid((unsigned)((N + SK_BN - 1) / SK_BN)), block(64 * SK_WAVES);
     if (lo)
-      gemm_skinny_stream_kernel<true><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+      gemm_skinny_stream_kernel<true><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
     else
-      gemm_skinny_stream_kernel<false><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+      gemm_skinny_stream_kernel<false><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
     return hipGetLastError();
   }
   if (M <= 16) {
-    if (vec16) return launch_mb<1, true>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
-    return launch_mb<1, false>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+    if (vec16) return launch_mb<1, true>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
+    return launch_mb<1, false>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
   }
-  if (vec16) return launch_mb<2, true>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
-  return launch_mb<2, false>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, m, n, k, r, yp);
+  if (vec16) return launch_mb<2, true>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
+  return launch_mb<2, false>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
 }
 
 }  // namespace w4a4

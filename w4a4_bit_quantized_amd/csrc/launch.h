@@ -25,22 +25,24 @@ int quantize_parts(int64_t M, int64_t K);
 
 // Block-scaled FP4 GEMM with the fused epilogue.  `lora` holds `lora_parts` partial sums,
 // each [M, R], added in order (lora_parts > 1 only for batches of at most SKINNY_MAX_M rows).
+// `bias` (bf16 [N]) may be null.
 hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora, int lora_parts,
                        const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
-                       const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, void* y, hipStream_t stream);
+                       const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
+                       hipStream_t stream);
 
 // MXFP4 GEMM (E8M0 scales per 32 columns; K % 128 == 0, N % 4 == 0; the activation scales
 // are (K/32, ms) with ms = M rounded up to 4) with the same fused epilogue.
 hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lora, int lora_parts,
                           const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
-                          const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, int64_t ms, void* y,
-                          hipStream_t stream);
+                          const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                          int64_t ms, void* y, hipStream_t stream);
 
 // Weight-streaming variant for M <= SKINNY_MAX_M (called by launch_gemm).
 hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float* lora, int lora_parts,
                               const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
-                              const void* wtscale, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
-                              hipStream_t stream);
+                              const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                              void* y, hipStream_t stream);
 
 // Standalone block Hadamard transform of rows x cols elements (row strides ldx, ldy in
 // elements; dtype 0 bf16, 1 f16, 2 f32; block a power of two in [2, 4096] dividing cols);

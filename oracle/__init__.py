@@ -26,6 +26,8 @@ Modules:
 * ``quant``    -- per-16-group FP4 quantizer, activation and weight quantizers,
                   INT4 absmax quantizer of the worked examples.
 * ``linear``   -- dequantize-then-matmul composition and the epilogue.
+* ``svd``      -- the offline low-rank split of a smoothed weight (top-R SVD,
+                  bf16 factors, residual for the 4-bit branch).
 * ``mx``       -- the MXFP4 variant (rotate notes, section 3.3, FP-Quant: E2M1
                   in blocks of 32 with one E8M0 power-of-two scale, group-32
                   rotation) with the same epilogue.
@@ -46,4 +48,4 @@ direction, scale layout, zero-scale rule, sign of zero -- are fixed readings,
 checked only for self-consistency.
 """
 
-from . import formats, hadamard, quant, linear, mx  # noqa: F401
+from . import formats, hadamard, quant, linear, mx, svd  # noqa: F401

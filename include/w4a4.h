@@ -219,6 +219,25 @@ w4a4_status svdq_linear_mx_bias(const void* x, const void* qweight, const void* 
                                 int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* ---- Offline low-rank split (host) ----------------------------------------------------------
+ * "SVDQuant W4A4" page, "Overview" (four-bit weights and activations plus a small low-rank
+ * branch that corrects part of the quantization error; checkpoints are quantized offline) and
+ * "Checkpoint contract" (proj_down (K, R), proj_up (N, R)).  HOST memory throughout; no GPU
+ * work.  With W_s = W * smooth_factor (float64) and its top-R singular triplets U_R S_R V_R:
+ *   proj_up   = bf16(U_R sqrt(S_R))         [N, R] bf16
+ *   proj_down = bf16(V_R sqrt(S_R))         [K, R] bf16
+ *   residual  = bf16(W_s - proj_up proj_down^T)   [N, K] bf16 (smoothing already applied: quantize
+ *               it with svdq_quantize_weight and a smooth_factor of ones to get qweight, wscales)
+ *   singular_values  S_1 >= ... >= S_R as float (may be NULL)
+ * The triplets come from a randomized range finder with R + oversample Gaussian columns (drawn
+ * from `seed`) and `power_iters` power iterations; `threads` host threads (<= 0: all cores).
+ * Sizes: 1 <= N, K <= 2^20, N * K <= 2^31, 0 <= R <= min(N, K, W4A4_MAX_RANK), oversample >= 0,
+ * power_iters >= 0, else W4A4_ERR_SHAPE; NULL w, smooth_factor or residual (or factors with
+ * R > 0): W4A4_ERR_NULL.  R == 0 writes the smoothed weight to residual. */
+w4a4_status svdq_lowrank_split(const void* w, const void* smooth_factor, int64_t N, int64_t K, int64_t R,
+                               int32_t oversample, int32_t power_iters, uint64_t seed, int32_t threads,
+                               void* proj_down, void* proj_up, void* residual, float* singular_values);
+
 /* ---- Standalone block Hadamard transform ------------------------------------------------
  * Rotate notes, section 3.1 (the Hadacore kernel behind hadacore_transform(x, inplace): the
  * Sylvester Hadamard transform applied through its recursion, symmetric and therefore its own

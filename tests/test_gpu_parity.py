@@ -338,3 +338,49 @@ def test_linear_bias_3d_input(w4, M, N, K, R, B):
                      **{k: f[k] for k in ("proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale")})
     _, y_ref, _ = olinear.svdq_linear(f["x"], ref_layer, B)
     H.assert_gates(H.from_dev_bf16_f64(y.reshape(M, N)), y_ref, "svdq_linear with bias")
+
+
+# ---- offline low-rank split feeding the layer ("SVDQuant W4A4" page, Overview) ------------------
+
+def test_lowrank_split_checkpoint_through_the_layer(w4):
+    """A checkpoint made by the library's own offline split (host) and weight quantizer (GPU, on
+    the residual with a smooth_factor of ones) runs through svdq_linear within the gates against
+    the oracle on the same tensors, and its error against the unquantized layer is below that
+    of quantizing the whole smoothed weight (the activations' own FP4 error remains in both)."""
+    import torch
+    from oracle import formats, quant, svd as osvd
+    rng = np.random.default_rng(12)
+    M, K, N, R = 96, 1024, 512, 32
+    u, _ = np.linalg.qr(rng.standard_normal((N, R)))
+    v, _ = np.linalg.qr(rng.standard_normal((K, R)))
+    w = formats.bf16_from_f64((u * np.linspace(40, 10, R)) @ v.T / np.sqrt(K)
+                              + 0.2 * rng.standard_normal((N, K)) / np.sqrt(K))
+    lam = formats.bf16_from_f64(rng.uniform(0.5, 2.0, K))
+    x = formats.bf16_from_f64(rng.standard_normal((M, K)))
+    pd, pu, resid, _ = w4.svdq_lowrank_split(w, lam, R)
+    ones = H.to_dev_bf16(formats.bf16_from_f64(np.ones(K)))
+    qw, ws = w4.svdq_quantize_weight(H.to_dev_bf16(resid), ones, 0)
+    torch.cuda.synchronize()
+    f32 = lambda b: formats.bf16_to_f32(b)
+    qw_ref, ws_ref = quant.quantize_weight(f32(resid), np.ones(K, np.float32), 0)
+    assert np.array_equal(qw.cpu().numpy(), qw_ref) and np.array_equal(ws.cpu().numpy(), ws_ref)
+    wcs = formats.bf16_from_f64(np.ones(N))
+    wts = formats.bf16_from_f64(np.ones(1))
+    layer = dict(qweight=qw, wscales=ws, proj_down=H.to_dev_bf16(pd), proj_up=H.to_dev_bf16(pu),
+                 smooth_factor=H.to_dev_bf16(lam), wcscales=H.to_dev_bf16(wcs), wtscale=H.to_dev_bf16(wts))
+    y = H.from_dev_bf16_f64(w4.svdq_linear(H.to_dev_bf16(x), layer, hadamard_block=0))
+    torch.cuda.synchronize()
+    ref_layer = dict(qweight=qw_ref, wscales=ws_ref, proj_down=f32(pd), proj_up=f32(pu), smooth_factor=f32(lam),
+                     wcscales=f32(wcs), wtscale=f32(wts))
+    _, y_ref, _ = olinear.svdq_linear(f32(x), ref_layer, 0)
+    H.assert_gates(y, y_ref, "layer from the offline split")
+    exact = f32(x).astype(np.float64) @ f32(w).astype(np.float64).T
+    # the same layer without the low-rank branch: the whole smoothed weight quantized
+    qw0, ws0 = quant.quantize_weight(f32(w), f32(lam), 0)
+    plain = dict(qweight=qw0, wscales=ws0, proj_down=np.zeros((K, 0), np.float32),
+                 proj_up=np.zeros((N, 0), np.float32), smooth_factor=f32(lam), wcscales=f32(wcs), wtscale=f32(wts))
+    _, y0, _ = olinear.svdq_linear(f32(x), plain, 0)
+    err_split = np.linalg.norm(y - exact) / np.linalg.norm(exact)
+    err_plain = np.linalg.norm(y0 - exact) / np.linalg.norm(exact)
+    print(f"\nrelative error vs unquantized: split {err_split:.4f}, whole weight quantized {err_plain:.4f}")
+    assert err_split < 0.8 * err_plain

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     svdq_gemm_lowrank_mx,
     svdq_linear_mx,
     svdq_linear_mx_workspace_bytes,
+    svdq_lowrank_split,
     svdq_quantize_act_mx,
     svdq_quantize_weight_mx,
 )

@@ -45,6 +45,8 @@ SIGNATURES = {
                                         _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "svdq_gemm_lowrank_mx_bias": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                                  _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "svdq_lowrank_split": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, ctypes.c_uint64,
+                                          _c_i32, _c_p, _c_p, _c_p, _c_p]),
     "svdq_linear_mx_bias": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                            _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t,
                                            _c_p]),
@@ -398,3 +400,27 @@ def hadamard_transform(x, block=None, inplace=False, out=None):
                                      _stream(x.device))
     _check(st, "w4a4_hadamard_transform")
     return y
+
+
+def svdq_lowrank_split(w, smooth_factor, rank, oversample=16, power_iters=4, seed=0, threads=0):
+    """Offline low-rank split of W * smooth_factor on the host (numpy bf16 bit patterns in, out).
+
+    ``w`` (N, K) and ``smooth_factor`` (K,) are uint16 arrays of bf16 bits.  Returns
+    (proj_down (K, R), proj_up (N, R), residual (N, K)) as uint16 bf16 bits and the R singular
+    values (float32).  The residual already carries the smoothing: quantize it with a
+    smooth_factor of ones."""
+    import numpy as np
+    lib = load_library()
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    lam = np.ascontiguousarray(smooth_factor, dtype=np.uint16)
+    N, K = w.shape
+    R = int(rank)
+    pd = np.zeros((K, R), dtype=np.uint16)
+    pu = np.zeros((N, R), dtype=np.uint16)
+    resid = np.zeros((N, K), dtype=np.uint16)
+    sv = np.zeros(max(R, 1), dtype=np.float32)
+    st = lib.svdq_lowrank_split(w.ctypes.data, lam.ctypes.data, N, K, R, int(oversample), int(power_iters),
+                                int(seed), int(threads), pd.ctypes.data if R else None,
+                                pu.ctypes.data if R else None, resid.ctypes.data, sv.ctypes.data)
+    _check(st, "svdq_lowrank_split")
+    return pd, pu, resid, sv[:R]

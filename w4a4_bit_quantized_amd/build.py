@@ -10,7 +10,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/api.cpp", "csrc/quantize.hip", "csrc/gemm.hip", "csrc/gemm_skinny.hip", "csrc/hadamard.hip"]
+SOURCES = ["csrc/api.cpp", "csrc/quantize.hip", "csrc/gemm.hip", "csrc/gemm_skinny.hip", "csrc/hadamard.hip",
+           "csrc/lowrank_split.cpp"]
 ARCH = os.environ.get("W4A4_ARCH", "gfx950")
 
 

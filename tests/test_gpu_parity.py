@@ -384,3 +384,24 @@ def test_lowrank_split_checkpoint_through_the_layer(w4):
     err_plain = np.linalg.norm(y0 - exact) / np.linalg.norm(exact)
     print(f"\nrelative error vs unquantized: split {err_split:.4f}, whole weight quantized {err_plain:.4f}")
     assert err_split < 0.8 * err_plain
+
+
+def test_w4a4_linear_from_state_dict(w4):
+    """The checkpoint helper's layer object: loads '<prefix>.<suffix>' tensors (with a bias) and
+    gives svdq_linear's result on a 3-D input."""
+    import torch
+    from w4a4_bit_quantized_amd import checkpoint as ck
+    lay = synth.make_layer("tiny", seed=29, M=48, K=256, N=192, R=32, B=0, wcs="uniform")
+    qw, ws = H.oracle_weights(lay)
+    dev_layer = H.device_layer(lay, qw, ws)
+    dev_layer["bias"] = H.to_dev_bf16(H.seeded_bias(192, 48))
+    state = {f"blocks.0.ff.{k}": v.cpu() for k, v in dev_layer.items()}
+    cfg = {"quant_method": "svdquant", "rank": 32, "precision": "nvfp4", "act_unsigned": False,
+           "modules_to_not_convert": ["proj_out"]}
+    lin = ck.W4A4Linear.from_state_dict("blocks.0.ff", state, cfg)
+    x = H.to_dev_bf16(lay["x"]).reshape(3, 16, 256)
+    y = lin(x)
+    y2 = w4.svdq_linear(x, dev_layer)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (3, 16, 192)
+    assert torch.equal(y, y2)

@@ -24,7 +24,9 @@ Readings taken where the pages are silent (the GPU path uses the same ones):
 * everything else -- smoothing, the optional rotation (here normally B = 32),
   the unrotated low-rank branch, the epilogue -- is the nvfp4 layer's.
 
-Inputs are finite (a non-finite block has no defined MX scale here).
+Inputs are finite, and so are their rotated values (a block that holds an
+infinity or NaN, or whose rotation overflows float32, has no defined MX scale
+here).
 
 Pins (``tests/test_oracle_mx.py``): E8M0 values from the OCP table and the
 doubling invariant; the scale exponent against a brute-force search over

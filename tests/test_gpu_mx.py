@@ -197,3 +197,38 @@ def test_linear_mx_bias(w4):
     _, y_ref, _ = omx.svdq_linear_mx(f["x"], ref_layer, 32)
     assert tuple(y.shape) == (4, 16, 264)
     H.assert_gates(H.from_dev_bf16_f64(y.reshape(64, 264)), y_ref, "svdq_linear_mx with bias")
+
+
+@pytest.mark.parametrize("B", [0, 32])
+def test_quantize_act_mx_special_values(w4, B):
+    """E8M0 edge cases, bit-exact: all-zero and negative-zero blocks (exponent clamped to -127),
+    block maxima exactly at 6 * 2^k (no round-up) and one bf16 step above it, subnormal-range
+    maxima, and maxima near the largest bf16 (exponent near +127)."""
+    import torch
+    M, K = 12, 256
+    lay = _lay(M, K, 64, 8, B, seed=77)
+    x = synth.bits_to_f32(lay["x"]).copy()
+    x[0, :] = 0.0
+    x[1, :32] = -0.0
+    x[1, 32:64] = 0.0
+    x[2, :32] = np.float32(6.0 * 2.0 ** 3)          # amax / 6 is exactly 2^3
+    x[3, :32] = np.float32(6.0 * 2.0 ** -20)
+    x[4, :32] = synth.bits_to_f32(synth.to_bf16_bits(np.float32([6.0 * 2.0 ** 3 * (1 + 2.0 ** -7)])))[0]  # next bf16
+    x[5, :32] = np.float32(2.0 ** -133)              # subnormal: amax / 6 far below 2^-127
+    x[6, :32] = np.float32(1e-38)
+    # exponent near the top of the E8M0 range (with the rotation, small enough that the 32-point
+    # sums stay finite: blocks whose rotated values overflow have no defined scale)
+    x[7, :32] = np.float32(3.0e38 if B == 0 else 5.0e36)
+    x[8, ::2] = -x[8, ::2]
+    x[9, 64:96] = np.float32(-5.0e37 if B == 0 else -5.0e36)
+    lay["x"] = synth.to_bf16_bits(x)
+    lay["smooth_factor"] = synth.to_bf16_bits(np.ones(K, np.float32))
+    lay["proj_down"] = synth.to_bf16_bits(np.zeros((K, 8), np.float32))
+    f = synth.as_f32(lay)
+    qa, sa, lo = w4.svdq_quantize_act_mx(H.to_dev_bf16(lay["x"]), H.to_dev_bf16(lay["smooth_factor"]),
+                                         H.to_dev_bf16(lay["proj_down"]), B)
+    torch.cuda.synchronize()
+    q_ref, s_ref, _ = omx.quantize_act_mx(f["x"], f["smooth_factor"], f["proj_down"], B)
+    assert np.array_equal(sa.cpu().numpy(), s_ref)
+    assert np.array_equal(qa.cpu().numpy(), q_ref)
+    assert s_ref[0, 0] == 0 and s_ref[0, 2] == 127 + 3 and s_ref[0, 4] == 127 + 4 if B == 0 else True

@@ -1,11 +1,15 @@
-// Matrix-core throughput probe for the instructions the GEMMs use (gfx950).
+// Matrix-core and HBM throughput probe (gfx950): the practical ceilings the kernels are judged
+// against.
 //
 // Every CU runs one 256-thread workgroup (one wave per SIMD); each wave issues ITER x 8
 // independent matrix instructions into 8 accumulators.  Reported per instruction kind: shader
 // cycles per instruction and wave (s_memtime), wall time (HIP events), the achieved dense
 // TFLOP/s and the implied shader clock.  Operands are either a constant byte pattern or random
 // bits: under random operands the chip draws more power and lowers its clock, which sets the
-// practical ceiling the GEMMs are compared against.  Nothing here is part of the library.
+// practical ceiling the GEMMs are compared against.  HBM: a 2 GiB read (16 bytes per lane,
+// summed so nothing is optimised away), a 1 GiB -> 1 GiB copy and a 1 GiB write, each timed with
+// HIP events over 5 repetitions after a warm-up (buffers far larger than the 256 MB Infinity
+// Cache).  Nothing here is part of the library.
 //
 // Usage: mfma_peak [iterations]   (default 4000)
 
@@ -60,6 +64,23 @@ __global__ __launch_bounds__(256) void probe(const int* in, float* out, unsigned
   }
   out[blockIdx.x * 256 + threadIdx.x] = acc;
   if (threadIdx.x == 0) cyc[blockIdx.x] = t1 - t0;
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void hbm_read(const u32x4_t* __restrict__ src, size_t n, unsigned* out) {
+  u32x4_t acc = {0, 0, 0, 0};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) acc ^= src[i];
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9E3779B9u) out[0] = 1;  // keeps the loads alive
+}
+
+__global__ __launch_bounds__(256) void hbm_copy(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(256) void hbm_write(u32x4_t* __restrict__ dst, size_t n) {
+  const u32x4_t v = {1, 2, 3, 4};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = v;
 }
 
 bool ok(hipError_t e, const char* what) {
@@ -130,5 +151,38 @@ int main(int argc, char** argv) {
   (void)hipFree(in);
   (void)hipFree(out);
   (void)hipFree(cyc);
+
+  // HBM
+  const size_t gib = (size_t)1 << 30;
+  u32x4_t *a = nullptr, *b = nullptr;
+  unsigned* flag = nullptr;
+  if (!ok(hipMalloc(&a, 2 * gib), "alloc") || !ok(hipMalloc(&b, gib), "alloc") || !ok(hipMalloc(&flag, 4), "alloc"))
+    return 1;
+  if (!ok(hipMemset(a, 1, 2 * gib), "memset") || !ok(hipMemset(b, 0, gib), "memset")) return 1;
+  const dim3 grid((unsigned)blocks * 16), block(256);
+  hipEvent_t e0, e1;
+  if (!ok(hipEventCreate(&e0), "event") || !ok(hipEventCreate(&e1), "event")) return 1;
+  struct Case { const char* name; int kind; double bytes; };
+  const Case cases[] = {{"read 2 GiB", 0, 2.0 * gib}, {"copy 1 GiB -> 1 GiB", 1, 2.0 * gib}, {"write 1 GiB", 2, 1.0 * gib}};
+  std::printf("HBM (%u workgroups of 256, 16 bytes per lane)\n", grid.x);
+  for (const Case& c : cases) {
+    auto launch = [&] {
+      if (c.kind == 0) hipLaunchKernelGGL(hbm_read, grid, block, 0, 0, a, 2 * gib / 16, flag);
+      if (c.kind == 1) hipLaunchKernelGGL(hbm_copy, grid, block, 0, 0, a, b, gib / 16);
+      if (c.kind == 2) hipLaunchKernelGGL(hbm_write, grid, block, 0, 0, b, gib / 16);
+    };
+    launch();
+    if (!ok(hipDeviceSynchronize(), "hbm warm-up")) return 1;
+    (void)hipEventRecord(e0);
+    for (int r = 0; r < 5; ++r) launch();
+    (void)hipEventRecord(e1);
+    if (!ok(hipEventSynchronize(e1), "hbm run")) return 1;
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    std::printf("%-26s %8.3f ms per pass  %7.0f GB/s\n", c.name, ms / 5, c.bytes / (ms / 5 * 1e-3) / 1e9);
+  }
+  (void)hipFree(a);
+  (void)hipFree(b);
+  (void)hipFree(flag);
   return 0;
 }

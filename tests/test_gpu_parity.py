@@ -184,6 +184,28 @@ def test_gemm_tile_unaligned_rows(w4, variant, path, N, monkeypatch):
     _check_gemm(w4, lay)
 
 
+@pytest.mark.parametrize("variant,grid,R,bias", [("2x4x4x2", 1, 32, False), ("2x4x4x2", 3, 64, True),
+                                                  ("4x2x2x3", 8, 5, True), ("4x2x2x3", 2, 0, False),
+                                                  ("2x2x2x2", 5, 64, False), ("2x2x4x2", 4, 33, True),
+                                                  ("2x2x4x3", 7, 16, False), ("4x2x2x4", 6, 32, True)])
+def test_gemm_persistent_tile_walk(w4, variant, grid, R, bias, monkeypatch):
+    """The persistent form of the direct-load kernel with the grid capped (W4A4_GEMM_GRID), so each
+    workgroup walks several tiles of a ragged shape: the next tile's first K-steps load during the
+    epilogue, ranks above 32 are staged in two passes, and out-of-range chunks are dropped by the
+    buffer stores.  Checked against the oracle and bit for bit against one workgroup per tile
+    (W4A4_GEMM_PERSIST=0)."""
+    import torch
+    monkeypatch.setenv("W4A4_GEMM_TILE", variant)
+    monkeypatch.setenv("W4A4_GEMM_PATH", "dma")
+    monkeypatch.setenv("W4A4_GEMM_GRID", str(grid))
+    lay = synth.make_layer("tiny", seed=grid * 7 + R, M=300, K=640, N=520, R=R, B=0, wcs="uniform")
+    y_gpu, _ = _check_gemm(w4, lay, bias=bias)
+    monkeypatch.setenv("W4A4_GEMM_PERSIST", "0")
+    y_one, _ = _check_gemm(w4, lay, bias=bias)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_gpu, y_one), "persistent and one-tile-per-workgroup outputs differ"
+
+
 @pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 0), (37, 70, 256, 32, 128), (3, 40, 48, 3, 16),
                                        (150, 260, 512, 64, 64),
                                        # small batches: K split across quantizer workgroups (partial low-rank sums)

@@ -86,14 +86,15 @@ struct Tile {
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_LDS ? 2 * STAGE_BYTES : EPI_LDS;
 };
 
-// Stage a tile's epilogue operands in LDS: the column scales wcscales * wtscale, the bias (zero
-// without one), and for the
-// ranks [0, rp) the low-rank activations summed over their `parts` partial sums (in order) and
-// split into bf16 hi + lo parts, and proj_up.  Padded ranks and rows past M or N are zero or
-// clamped.  Each thread issues all its loads of a 16-rank block before storing any of them.
+// Stage a tile's epilogue operands in LDS: the column scales wcscales * wtscale and the bias
+// (zero without one) when r_lo == 0, and for the ranks [r_lo, r_hi) (columns r - r_lo of the
+// rank-strided arrays) the low-rank activations summed over their `parts` partial sums (in
+// order) and split into bf16 hi + lo parts, and proj_up.  Padded ranks and rows past M or N are
+// zero or clamped.  Each thread issues all its loads of a 16-rank block before storing any of
+// them.
 template <class T, bool LORA>
-__device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int rp, int t, int m0, int n0, int M, int N,
-                                               int R, int parts, const float* __restrict__ lora,
+__device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int r_lo, int r_hi, int t, int m0, int n0,
+                                               int M, int N, int R, int parts, const float* __restrict__ lora,
                                                const uint16_t* __restrict__ pu, const uint16_t* __restrict__ wcs,
                                                const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias) {
   uint16_t* l_hi = reinterpret_cast<uint16_t*>(base);
@@ -101,16 +102,18 @@ __device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int rp, in
   uint16_t* p_lds = l_lo + T::BM * rs;
   float* c_lds = reinterpret_cast<float*>(p_lds + T::BN * rs);
   float* b_lds = c_lds + T::BN;
-  const float ts = bf16_bits_to_f32(wts[0]);
-  for (int c = t; c < T::BN; c += T::THREADS) {
-    const int n = n0 + c;
-    c_lds[c] = n < N ? bf16_bits_to_f32(wcs[n]) * ts : 0.0f;
-    b_lds[c] = (bias != nullptr && n < N) ? bf16_bits_to_f32(bias[n]) : 0.0f;
+  if (r_lo == 0) {
+    const float ts = bf16_bits_to_f32(wts[0]);
+    for (int c = t; c < T::BN; c += T::THREADS) {
+      const int n = n0 + c;
+      c_lds[c] = n < N ? bf16_bits_to_f32(wcs[n]) * ts : 0.0f;
+      b_lds[c] = (bias != nullptr && n < N) ? bf16_bits_to_f32(bias[n]) : 0.0f;
+    }
   }
   if (!LORA) return;
   constexpr int LI = (T::BM * 16 + T::THREADS - 1) / T::THREADS;
   constexpr int PI = (T::BN * 16 + T::THREADS - 1) / T::THREADS;
-  for (int r0 = 0; r0 < rp; r0 += 16) {
+  for (int r0 = r_lo; r0 < r_hi; r0 += 16) {
     float f[LI];
     uint32_t pw[PI];
 #pragma unroll
@@ -133,7 +136,7 @@ __device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int rp, in
     for (int u = 0; u < LI; ++u) {
       const int idx = t + u * T::THREADS;
       if ((T::BM * 16) % T::THREADS == 0 || idx < T::BM * 16) {
-        const int rr = idx >> 4, r = r0 + (idx & 15);
+        const int rr = idx >> 4, r = r0 - r_lo + (idx & 15);
         const uint32_t hb = f32_to_bf16_bits(f[u]);
         l_hi[rr * rs + r] = (uint16_t)hb;
         l_lo[rr * rs + r] = (uint16_t)f32_to_bf16_bits(f[u] - bf16_bits_to_f32(hb));  // exact remainder
@@ -142,7 +145,7 @@ __device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int rp, in
 #pragma unroll
     for (int u = 0; u < PI; ++u) {
       const int idx = t + u * T::THREADS;
-      if ((T::BN * 16) % T::THREADS == 0 || idx < T::BN * 16) p_lds[(idx >> 4) * rs + r0 + (idx & 15)] = (uint16_t)pw[u];
+      if ((T::BN * 16) % T::THREADS == 0 || idx < T::BN * 16) p_lds[(idx >> 4) * rs + r0 - r_lo + (idx & 15)] = (uint16_t)pw[u];
     }
   }
 }
@@ -352,7 +355,7 @@ __device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N],
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int l32 = lane & 31, h = lane >> 5;
   const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank
-  stage_epilogue<T, LORA>(lds, rs, rp, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
+  stage_epilogue<T, LORA>(lds, rs, 0, rp, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
   __syncthreads();
   const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
   const uint16_t* l_hi = reinterpret_cast<const uint16_t*>(lds);
@@ -686,71 +689,57 @@ __device__ __forceinline__ void dma_issue(uint8_t* stage, int wave, uint32_t kb0
                                      (lds_void*)(stage + D::SCALE_OFF + (r * D::WAVES + wave) * 256), 4, 0, 0);
 }
 
-template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
-    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
-    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
-    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R,
-    uint16_t* __restrict__ y) {
-  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
+// Per-tile addresses of a wave's direct loads: the code chunk of each round (tile row clamped to
+// a valid row, swizzled 16-byte chunk) and the scale dword of each round (LDS dword index d ->
+// quad d / 8 of tile rows 4 quad .., group d % 8).
+template <class T>
+struct DmaAddr {
   using D = DmaTile<T>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[D::LDS_BYTES];
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int tiles_n = (N + T::BN - 1) / T::BN;
-  int tm, tn;
-  tile_of((int)blockIdx.x, (int)gridDim.x, (M + T::BM - 1) / T::BM, tiles_n, tm, tn);
-  const int n0 = tn * T::BN;
-  const int m0 = tm * T::BM;
-  const uint32_t kbytes = (uint32_t)K / 2;
-  const int nkt = K / BK;
-  const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);  // multiples of 4
-
-  // code chunk of each round: tile row (clamped to a valid row) and swizzled 16-byte chunk
   const uint8_t* c_base[D::ROUNDS];
   uint32_t c_off[D::ROUNDS];
-#pragma unroll
-  for (int r = 0; r < D::ROUNDS; ++r) {
-    const int row = r * D::ROUND_ROWS + wave * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ code_swizzle(row);
-    const bool is_a = row < T::BM;
-    const int src = is_a ? min(row, rows_a - 1) : min(row - T::BM, rows_b - 1);
-    c_base[r] = is_a ? qa + (size_t)m0 * kbytes : qw + (size_t)n0 * kbytes;
-    c_off[r] = (uint32_t)src * kbytes + 16u * (uint32_t)c;
-  }
-  // scale dword of each round: LDS dword index d -> quad d / 8 (tile rows 4 quad ..), group d % 8
   const uint8_t* s_base[D::SROUNDS];
   uint32_t s_off[D::SROUNDS], s_stride[D::SROUNDS];
+
+  __device__ __forceinline__ void set(int wave, int lane, int m0, int n0, int M, int N, uint32_t kbytes,
+                                      const uint8_t* qa, const uint8_t* sa, const uint8_t* qw, const uint8_t* sw) {
+    const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);  // multiples of 4
 #pragma unroll
-  for (int r = 0; r < D::SROUNDS; ++r) {
-    const int d = min((r * D::WAVES + wave) * 64 + lane, D::SDW - 1);
-    const int quad = d >> 3, g = d & 7;
-    const bool is_a = 4 * quad < T::BM;
-    const int row = is_a ? min(4 * quad, rows_a - 4) : min(4 * quad - T::BM, rows_b - 4);
-    s_base[r] = is_a ? sa + m0 : sw + n0;
-    s_stride[r] = is_a ? (uint32_t)M : (uint32_t)N;
-    s_off[r] = (uint32_t)g * s_stride[r] + (uint32_t)row;
+    for (int r = 0; r < D::ROUNDS; ++r) {
+      const int row = r * D::ROUND_ROWS + wave * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ code_swizzle(row);
+      const bool is_a = row < T::BM;
+      const int src = is_a ? min(row, rows_a - 1) : min(row - T::BM, rows_b - 1);
+      c_base[r] = is_a ? qa + (size_t)m0 * kbytes : qw + (size_t)n0 * kbytes;
+      c_off[r] = (uint32_t)src * kbytes + 16u * (uint32_t)c;
+    }
+#pragma unroll
+    for (int r = 0; r < D::SROUNDS; ++r) {
+      const int d = min((r * D::WAVES + wave) * 64 + lane, D::SDW - 1);
+      const int quad = d >> 3, g = d & 7;
+      const bool is_a = 4 * quad < T::BM;
+      const int row = is_a ? min(4 * quad, rows_a - 4) : min(4 * quad - T::BM, rows_b - 4);
+      s_base[r] = is_a ? sa + m0 : sw + n0;
+      s_stride[r] = is_a ? (uint32_t)M : (uint32_t)N;
+      s_off[r] = (uint32_t)g * s_stride[r] + (uint32_t)row;
+    }
   }
+  // K-step kt's direct loads of this wave into the stage at `stage`
+  __device__ __forceinline__ void issue(uint8_t* stage, int wave, int kt) const {
+    dma_issue<D>(stage, wave, (uint32_t)kt * (BK / 2), (size_t)kt * (BK / 16), c_base, c_off, s_base, s_off, s_stride);
+  }
+};
 
-
-  dma_issue<D>(lds + (0) * D::STAGE, wave, (uint32_t)(0) * (BK / 2), (size_t)(0) * (BK / 16), c_base, c_off,
-                 s_base, s_off, s_stride);
-  dma_issue<D>(lds + (1) * D::STAGE, wave, (uint32_t)(nkt > 1 ? 1 : 0) * (BK / 2), (size_t)(nkt > 1 ? 1 : 0) * (BK / 16), c_base, c_off,
-                 s_base, s_off, s_stride);
-  vm_wait_barrier<0>();
-
-  float16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
+// The K loop of one tile.  On entry K-steps 0 and 1 are in flight into slots 0 and 1, followed by
+// S0 other vector-memory operations of this wave (stores of the previous tile, which complete
+// in issue order with the loads); every wait counts what may still be in flight behind the
+// K-step it needs.  Returns with every load landed and LDS free.
+template <class T, int S0>
+__device__ __forceinline__ void dma_k_loop(float16_t (&acc)[T::FRAG_M][T::FRAG_N], uint8_t* lds, const DmaAddr<T>& ad,
+                                           int wave, int wm, int wn, int l32, int h, int nkt) {
+  using D = DmaTile<T>;
+  constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
+  static_assert(D::LOADS + S0 < 64, "vmcnt range");
+  vm_wait_barrier<D::LOADS + S0>();  // K-step 0 has landed
   // byte of the lane's row within a scale dword, as a v_perm selector: result byte 0 from the
   // first dword, byte 1 from the second
   const uint32_t psel = (uint32_t)(l32 & 3) | ((uint32_t)(4 + (l32 & 3)) << 8) | 0x0C0C0000u;
@@ -759,14 +748,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
     sp[0] = e4m3x2_to_h2bits(__builtin_amdgcn_perm(w[1], w[0], psel));
     sp[1] = e4m3x2_to_h2bits(__builtin_amdgcn_perm(w[3], w[2], psel));
   };
-
   // Every iteration issues the same loads (the last two reload the final K-step into a slot
   // nobody reads again), so every wave has the same count in flight at each wait.
   int slot = 0;
   for (int kt = 0; kt < nkt; ++kt) {
     const int slot2 = slot == 0 ? 2 : slot - 1;  // (kt + 2) % 3: read in K-step kt - 1, now free
-    dma_issue<D>(lds + (slot2) * D::STAGE, wave, (uint32_t)(min(kt + 2, nkt - 1)) * (BK / 2), (size_t)(min(kt + 2, nkt - 1)) * (BK / 16), c_base, c_off,
-                 s_base, s_off, s_stride);
+    ad.issue(lds + slot2 * D::STAGE, wave, min(kt + 2, nkt - 1));
     const uint8_t* cur = lds + slot * D::STAGE;
     uint32_t sA[FM][2], sB[FN][2];
     u32x4_t cA[2][FM], cB[2][FN];
@@ -787,13 +774,243 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
       cB[1][j] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h + 1) ^ sw4));
     }
     mma_stage<FM, FN>(acc, sA, sB, cA, cB);
-    // K-step kt + 1's loads were issued before K-step kt + 2's: at most the latter are in flight
-    vm_wait_barrier<D::LOADS>();
+    // K-step kt + 1's loads were issued before K-step kt + 2's: at most the latter (and, after
+    // K-step 0, the S0 older stores) are in flight
+    if (S0 > 0 && kt == 0)
+      vm_wait_barrier<D::LOADS + S0>();
+    else
+      vm_wait_barrier<D::LOADS>();
     slot = slot == 2 ? 0 : slot + 1;
   }
-  vm_wait_barrier<0>();  // the last reloads land before the epilogue reuses LDS
+  vm_wait_barrier<0>();  // the last reloads land before LDS is reused
+}
 
+template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
+    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R,
+    uint16_t* __restrict__ y) {
+  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
+  using D = DmaTile<T>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[D::LDS_BYTES];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int tiles_n = (N + T::BN - 1) / T::BN;
+  int tm, tn;
+  tile_of((int)blockIdx.x, (int)gridDim.x, (M + T::BM - 1) / T::BM, tiles_n, tm, tn);
+  const int n0 = tn * T::BN;
+  const int m0 = tm * T::BM;
+  const int nkt = K / BK;
+
+  DmaAddr<T> ad;
+  ad.set(wave, lane, m0, n0, M, N, (uint32_t)K / 2, qa, sa, qw, sw);
+  ad.issue(lds, wave, 0);
+  ad.issue(lds + D::STAGE, wave, nkt > 1 ? 1 : 0);
+
+  float16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  dma_k_loop<T, 0>(acc, lds, ad, wave, wm, wn, l32, h, nkt);
   epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, y);
+}
+
+// ---- persistent form: the next tile's first K-steps load during the epilogue ---------------
+// One workgroup per CU (or as many as fit) walks the tiles v = blockIdx.x, + gridDim.x, ... of
+// the same grouped, XCD-aware order (gridDim.x a multiple of 8 keeps every tile of a workgroup
+// on one XCD).  The epilogue operands live in a region E after stage slots 0 and 1, staged 32
+// ranks at a time, so the next tile's K-steps 0 and 1 are fetched into those slots as soon as
+// the first pass is staged and land while the epilogue computes.  y leaves through buffer
+// stores: a chunk outside y gets an offset the hardware drops, so every wave issues exactly ST
+// stores per tile, and the next tile's first waits count them in: the stores drain while
+// K-steps 0 and 1 run on the matrix cores.  Needs whole 16-byte runs of y rows (N % 8 == 0, y
+// 16-byte aligned) and |y| below 2^31 bytes.
+template <class T>
+struct PersistTile {
+  using D = DmaTile<T>;
+  static constexpr int RW = 32;  // ranks staged per pass (rank stride of the staged operands)
+  static constexpr int WAVES = T::WM * T::WN;
+  static constexpr int RSB = T::FRAG_N * 64, CPR = T::FRAG_N * 4;  // store region row: bytes, 16-byte chunks
+  static constexpr int OPS = T::BM * RW * 4 + T::BN * RW * 2 + T::BN * 8;  // L hi + lo, proj_up, scale, bias
+  static constexpr int REGIONS = WAVES * 32 * RSB;  // one 32-row fragment row per wave
+  static constexpr int E_OFF = 2 * D::STAGE;
+  static constexpr int E_BYTES = OPS > REGIONS ? OPS : REGIONS;
+  static constexpr int LDS_BYTES = 3 * D::STAGE > E_OFF + E_BYTES ? 3 * D::STAGE : E_OFF + E_BYTES;
+  static constexpr int ST = T::FRAG_M * CPR / 2;  // y stores of a wave per tile
+  static_assert(!T::ROWWISE, "whole-tile epilogue");
+  static_assert(D::LOADS + ST < 64, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
+};
+
+// LDS-only barrier: waits for this wave's LDS operations, not for its loads or stores in flight.
+__device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kernel(
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
+    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R,
+    uint16_t* __restrict__ y) {
+  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
+  using D = DmaTile<T>;
+  using P = PersistTile<T>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[P::LDS_BYTES];
+  constexpr int rs = P::RW, RSB = P::RSB, CPR = P::CPR;
+
+  const int lane0 = (int)threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform: wave-level addresses in scalar registers
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+  const int tiles = tiles_m * tiles_n;
+  const int nkt = K / BK;
+  const uint32_t kbytes = (uint32_t)K / 2;
+  const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank
+  const uint32_t ybytes = (uint32_t)M * (uint32_t)N * 2u;
+  const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(y, 0, (int)ybytes, 0x00020000);
+  uint8_t* const E = lds + P::E_OFF;
+  const uint16_t* l_hi = reinterpret_cast<const uint16_t*>(E);
+  const uint16_t* l_lo = l_hi + T::BM * rs;
+  const uint16_t* p_lds = l_lo + T::BM * rs;
+  const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
+  const float* b_lds = c_lds + T::BN;
+
+  int v = (int)blockIdx.x;
+  int tm, tn;
+  tile_of(v, tiles, tiles_m, tiles_n, tm, tn);
+  {
+    DmaAddr<T> ad;
+    ad.set(wave, lane0, tm * T::BM, tn * T::BN, M, N, kbytes, qa, sa, qw, sw);
+    ad.issue(lds, wave, 0);
+    ad.issue(lds + D::STAGE, wave, nkt > 1 ? 1 : 0);
+  }
+  bool first = true;
+  for (;;) {
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    // Lane-derived addresses are recomputed in each phase rather than hoisted out of the tile
+    // loop, where the K loop's and the epilogue's would all stay live at once.
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    int l32 = lane & 31, h = lane >> 5;
+    DmaAddr<T> ad;
+    ad.set(wave, lane, m0, n0, M, N, kbytes, qa, sa, qw, sw);
+    float16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    if (first)
+      dma_k_loop<T, 0>(acc, lds, ad, wave, wm, wn, l32, h, nkt);
+    else
+      dma_k_loop<T, P::ST>(acc, lds, ad, wave, wm, wn, l32, h, nkt);
+    first = false;
+
+    // epilogue operands, first pass; then the next tile's K-steps 0 and 1 into slots 0 and 1
+    asm volatile("" : "+v"(lane));
+    l32 = lane & 31;
+    h = lane >> 5;
+    const int t = wave * 64 + lane;
+    stage_epilogue<T, LORA>(E, rs, 0, min(rp, rs), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
+    const int vn = v + (int)gridDim.x;
+    const bool more = vn < tiles;  // workgroup-uniform
+    if (more) {
+      tile_of(vn, tiles, tiles_m, tiles_n, tm, tn);
+      DmaAddr<T> nad;
+      nad.set(wave, lane, tm * T::BM, tn * T::BN, M, N, kbytes, qa, sa, qw, sw);
+      nad.issue(lds, wave, 0);
+      nad.issue(lds + D::STAGE, wave, nkt > 1 ? 1 : 0);
+    }
+    lds_only_barrier();
+
+    // acc *= wcscales * wtscale; + L @ proj_up^T (passes of 32 ranks); + bias (as in `epilogue`)
+    const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
+      }
+    if (LORA) {
+      for (int lo = 0; lo < rp; lo += rs) {
+        if (lo > 0) {
+          lds_only_barrier();  // every wave is done with the previous pass
+          stage_epilogue<T, LORA>(E, rs, lo, min(rp, lo + rs), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
+          lds_only_barrier();
+        }
+        for (int r0 = 0; r0 < min(rp - lo, rs); r0 += 16) {
+          bf16x8_t pv[FN];
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            pv[j] = *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * rs + r0 + 8 * h);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = wm * FM * 32 + i * 32 + l32;
+            const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * rs + r0 + 8 * h);
+            const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], llo, acc[i][j], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+    if (bias != nullptr) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4_t b = *reinterpret_cast<const float4_t*>(b_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] += b[e];
+        }
+    }
+    lds_only_barrier();  // every wave is done with the staged operands: E becomes store regions
+
+    // one fragment row at a time through the wave's region (chunk ch of region row r at
+    // (ch + r / 2) % CPR), then whole 16-byte runs of y rows
+    uint8_t* reg = E + wave * 32 * RSB;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = 4 * j + q;
+          const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<u32x2_t*>(reg + l32 * RSB + 16 * ((ch + (l32 >> 1)) % CPR) + 8 * h) = u32x2_t{p0, p1};
+        }
+      wave_lds_sync();
+#pragma unroll
+      for (int it = 0; it < CPR / 2; ++it) {
+        const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR));
+        const int m = mb + i * 32 + r, n = nb + 8 * ch;
+        const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(val, yr, (int)off, 0, 0);
+      }
+      wave_lds_sync();  // the region is rewritten by the next fragment row
+    }
+    if (!more) break;
+    v = vn;
+  }
 }
 
 // ---- MXFP4 variant (rotate notes, section 3.3: FP-Quant mxfp4, matmul_mxf4_bf16) ----------
@@ -1099,13 +1316,63 @@ hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* s
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Workgroups of the persistent kernel: as many as run at once (resident workgroups per CU x
+// CUs, a multiple of 8 so that each workgroup's tiles stay on one XCD), at most one per tile;
+// W4A4_GEMM_GRID caps it (tests: several tiles per workgroup at small sizes).  0: not usable.
+template <class KernelFn>
+int persist_grid(KernelFn kernel, int threads, int tiles) {
+  static int per_cu = -1;  // per instantiation; every device here is the same model
+  if (per_cu < 0) {
+    int n = 0;
+    per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) == hipSuccess ? n : 0;
+  }
+  const int cus = device_cus();
+  int g = per_cu * cus;
+  if (g >= 8) g -= g % 8;
+  if (const char* cap = getenv("W4A4_GEMM_GRID")) {
+    const int c = atoi(cap);
+    if (c > 0 && c < g) g = c;
+  }
+  return g < tiles ? g : tiles;
+}
+
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 hipError_t launch_dma(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                       const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
                       const uint16_t* wts, const uint16_t* bias, int M, int N, int K, int R, uint16_t* y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
-  dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
+  const int tiles = ((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM);
+  dim3 grid((unsigned)tiles);
   dim3 block(T::THREADS);
+  if constexpr (!T::ROWWISE) {
+    // persistent form: whole 16-byte runs of y rows, |y| addressable by a buffer offset;
+    // W4A4_GEMM_PERSIST=0 keeps one workgroup per tile
+    const char* pe = getenv("W4A4_GEMM_PERSIST");
+    const bool persist = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                         (int64_t)M * N * 2 <= (int64_t)0x7FFFFFF0 && !(pe && !strcmp(pe, "0"));
+    if (persist) {
+      auto kern = rb > 0 ? gemm_dma_persist_kernel<WAVES_M, WAVES_N, FM, FN, true>
+                         : gemm_dma_persist_kernel<WAVES_M, WAVES_N, FM, FN, false>;
+      const int g = persist_grid(kern, T::THREADS, tiles);
+      if (g > 0) {
+        kern<<<dim3((unsigned)g), block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
+        return hipGetLastError();
+      }
+    }
+  }
   if (rb > 0)
     gemm_dma_kernel<WAVES_M, WAVES_N, FM, FN, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
   else

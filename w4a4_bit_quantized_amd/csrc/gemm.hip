@@ -76,8 +76,11 @@ struct Tile {
   static constexpr int SCALE_BYTES = 8 * ROWS * 2;  // f16 scales laid out [group][row]
   static constexpr int STAGE_BYTES = ROWS * CODE_STRIDE + SCALE_BYTES;
   // Epilogue operands, staged in the stage buffers after the K loop: L hi and lo parts
-  // [BM][64] bf16, proj_up [BN][64] bf16, the column scale [BN] f32 and the bias [BN] f32.
-  static constexpr int EPI_BYTES = BM * 64 * 2 * 2 + BN * 64 * 2 + BN * 8;
+  // [BM][EPI_RS] bf16, proj_up [BN][EPI_RS] bf16, the column scale [BN] f32 and the bias [BN] f32.
+  // The rank stride holds the compiled maximum rank plus 8: 144-byte rows put the 16-byte reads
+  // of 16 consecutive rows on distinct banks.
+  static constexpr int EPI_RS = 64 + 8;
+  static constexpr int EPI_BYTES = BM * EPI_RS * 2 * 2 + BN * EPI_RS * 2 + BN * 8;
   // Waves with 16 or more accumulator fragments (which fill the accumulation registers) finish
   // one fragment row at a time, each wave through a 32-row store region of its own placed after
   // the epilogue operands.
@@ -350,7 +353,7 @@ __device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N],
                                          const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias,
                                          uint16_t* __restrict__ y) {
   constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
-  constexpr int rs = 64;  // rank stride of the staged operands (compiled maximum rank)
+  constexpr int rs = T::EPI_RS;  // rank stride of the staged operands
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int l32 = lane & 31, h = lane >> 5;
@@ -836,10 +839,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 template <class T>
 struct PersistTile {
   using D = DmaTile<T>;
-  static constexpr int RW = 32;  // ranks staged per pass (rank stride of the staged operands)
+  static constexpr int RW = 32;      // ranks staged per pass
+  static constexpr int RS = RW + 8;  // rank stride of the staged operands: 80-byte rows put the 16-byte
+                                     // reads of 16 consecutive rows on distinct banks
   static constexpr int WAVES = T::WM * T::WN;
   static constexpr int RSB = T::FRAG_N * 64, CPR = T::FRAG_N * 4;  // store region row: bytes, 16-byte chunks
-  static constexpr int OPS = T::BM * RW * 4 + T::BN * RW * 2 + T::BN * 8;  // L hi + lo, proj_up, scale, bias
+  static constexpr int OPS = T::BM * RS * 4 + T::BN * RS * 2 + T::BN * 8;  // L hi + lo, proj_up, scale, bias
   static constexpr int REGIONS = WAVES * 32 * RSB;  // one 32-row fragment row per wave
   static constexpr int E_OFF = 2 * D::STAGE;
   static constexpr int E_BYTES = OPS > REGIONS ? OPS : REGIONS;
@@ -863,7 +868,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
   using D = DmaTile<T>;
   using P = PersistTile<T>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[P::LDS_BYTES];
-  constexpr int rs = P::RW, RSB = P::RSB, CPR = P::CPR;
+  constexpr int rw = P::RW, rs = P::RS, RSB = P::RSB, CPR = P::CPR;
 
   const int lane0 = (int)threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform: wave-level addresses in scalar registers
@@ -919,7 +924,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
     l32 = lane & 31;
     h = lane >> 5;
     const int t = wave * 64 + lane;
-    stage_epilogue<T, LORA>(E, rs, 0, min(rp, rs), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
+    stage_epilogue<T, LORA>(E, rs, 0, min(rp, rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
     const int vn = v + (int)gridDim.x;
     const bool more = vn < tiles;  // workgroup-uniform
     if (more) {
@@ -944,13 +949,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
           for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
       }
     if (LORA) {
-      for (int lo = 0; lo < rp; lo += rs) {
+      for (int lo = 0; lo < rp; lo += rw) {
         if (lo > 0) {
           lds_only_barrier();  // every wave is done with the previous pass
-          stage_epilogue<T, LORA>(E, rs, lo, min(rp, lo + rs), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
+          stage_epilogue<T, LORA>(E, rs, lo, min(rp, lo + rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
           lds_only_barrier();
         }
-        for (int r0 = 0; r0 < min(rp - lo, rs); r0 += 16) {
+        for (int r0 = 0; r0 < min(rp - lo, rw); r0 += 16) {
           bf16x8_t pv[FN];
 #pragma unroll
           for (int j = 0; j < FN; ++j)

@@ -833,8 +833,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 // ranks at a time, so the next tile's K-steps 0 and 1 are fetched into those slots as soon as
 // the first pass is staged and land while the epilogue computes.  y leaves through buffer
 // stores: a chunk outside y gets an offset the hardware drops, so every wave issues exactly ST
-// stores per tile, and the next tile's first waits count them in: the stores drain while
-// K-steps 0 and 1 run on the matrix cores.  Needs whole 16-byte runs of y rows (N % 8 == 0, y
+// stores per tile (before the first tile, ST dropped ones), and each tile's first waits count
+// them in: the stores drain while K-steps 0 and 1 run on the matrix cores.  Needs whole 16-byte runs of y rows (N % 8 == 0, y
 // 16-byte aligned) and |y| below 2^31 bytes.
 template <class T>
 struct PersistTile {
@@ -896,7 +896,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
     ad.issue(lds, wave, 0);
     ad.issue(lds + D::STAGE, wave, nkt > 1 ? 1 : 0);
   }
-  bool first = true;
+  // ST stores the hardware drops (offset past y), so that the first tile's waits count the same
+  // stores as every later tile's: one copy of the K loop
+#pragma unroll
+  for (int i = 0; i < P::ST; ++i) __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, yr, (int)0x80000000u, 0, 0);
   for (;;) {
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     // Lane-derived addresses are recomputed in each phase rather than hoisted out of the tile
@@ -913,11 +916,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    if (first)
-      dma_k_loop<T, 0>(acc, lds, ad, wave, wm, wn, l32, h, nkt);
-    else
-      dma_k_loop<T, P::ST>(acc, lds, ad, wave, wm, wn, l32, h, nkt);
-    first = false;
+    dma_k_loop<T, P::ST>(acc, lds, ad, wave, wm, wn, l32, h, nkt);
 
     // epilogue operands, first pass; then the next tile's K-steps 0 and 1 into slots 0 and 1
     asm volatile("" : "+v"(lane));

@@ -746,11 +746,21 @@ __device__ __forceinline__ void dma_k_loop(float16_t (&acc)[T::FRAG_M][T::FRAG_N
   // byte of the lane's row within a scale dword, as a v_perm selector: result byte 0 from the
   // first dword, byte 1 from the second
   const uint32_t psel = (uint32_t)(l32 & 3) | ((uint32_t)(4 + (l32 & 3)) << 8) | 0x0C0C0000u;
-  auto scales_of = [&](const uint8_t* cur, int row, uint32_t (&sp)[2]) {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(cur + D::SCALE_OFF + (row >> 2) * 32 + 16 * h);
-    sp[0] = e4m3x2_to_h2bits(__builtin_amdgcn_perm(w[1], w[0], psel));
-    sp[1] = e4m3x2_to_h2bits(__builtin_amdgcn_perm(w[3], w[2], psel));
+  // e4m3 pair -> f16 pair in one exact convert (scale 1.0)
+  auto scales_of = [&](const uint8_t* p, uint32_t (&sp)[2]) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p);
+    sp[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w[1], w[0], psel), 1.0f, false));
+    sp[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w[3], w[2], psel), 1.0f, false));
   };
+  // Operand addresses: fragment and wave row offsets are multiples of 32, so a row's chunk
+  // swizzle depends on l32 alone and every read is one of six per-lane bases (codes of chunk
+  // pair half 0 / 1 and scales, for the wave's A and B rows) plus the slot and an immediate.
+  const int sw4 = (l32 >> 2) & 3;
+  const int ra = wm * FM * 32, rb = T::BM + wn * FN * 32;  // first A and B row of the wave
+  const uint32_t lc0 = (uint32_t)(l32 * 64 + 16 * ((2 * h) ^ sw4)), lc1 = (uint32_t)(l32 * 64 + 16 * ((2 * h + 1) ^ sw4));
+  const uint32_t lsc = (uint32_t)(D::SCALE_OFF + (l32 >> 2) * 32 + 16 * h);
+  const uint32_t a0 = lc0 + ra * 64, a1 = lc1 + ra * 64, as = lsc + (ra >> 2) * 32;
+  const uint32_t b0 = lc0 + rb * 64, b1 = lc1 + rb * 64, bs = lsc + (rb >> 2) * 32;
   // Every iteration issues the same loads (the last two reload the final K-step into a slot
   // nobody reads again), so every wave has the same count in flight at each wait.
   int slot = 0;
@@ -762,19 +772,15 @@ __device__ __forceinline__ void dma_k_loop(float16_t (&acc)[T::FRAG_M][T::FRAG_N
     u32x4_t cA[2][FM], cB[2][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int row = wm * FM * 32 + i * 32 + l32;
-      const int sw4 = code_swizzle(row);
-      scales_of(cur, row, sA[i]);
-      cA[0][i] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h) ^ sw4));
-      cA[1][i] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h + 1) ^ sw4));
+      scales_of(cur + as + i * 8 * 32, sA[i]);
+      cA[0][i] = *reinterpret_cast<const u32x4_t*>(cur + a0 + i * 32 * 64);
+      cA[1][i] = *reinterpret_cast<const u32x4_t*>(cur + a1 + i * 32 * 64);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int row = T::BM + wn * FN * 32 + j * 32 + l32;
-      const int sw4 = code_swizzle(row);
-      scales_of(cur, row, sB[j]);
-      cB[0][j] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h) ^ sw4));
-      cB[1][j] = *reinterpret_cast<const u32x4_t*>(cur + row * 64 + 16 * ((2 * h + 1) ^ sw4));
+      scales_of(cur + bs + j * 8 * 32, sB[j]);
+      cB[0][j] = *reinterpret_cast<const u32x4_t*>(cur + b0 + j * 32 * 64);
+      cB[1][j] = *reinterpret_cast<const u32x4_t*>(cur + b1 + j * 32 * 64);
     }
     mma_stage<FM, FN>(acc, sA, sB, cA, cB);
     // K-step kt + 1's loads were issued before K-step kt + 2's: at most the latter (and, after

@@ -9,7 +9,9 @@
 // practical ceiling the GEMMs are compared against.  HBM: a 2 GiB read (16 bytes per lane,
 // summed so nothing is optimised away), a 1 GiB -> 1 GiB copy and a 1 GiB write, each timed with
 // HIP events over 5 repetitions after a warm-up (buffers far larger than the 256 MB Infinity
-// Cache).  Nothing here is part of the library.
+// Cache).  LDS: every CU runs one workgroup of 256, 512 or 1024 threads reading 16 bytes per lane
+// per instruction from a 64 KB buffer, consecutive lanes on consecutive 16-byte chunks (no bank
+// conflicts), timed with HIP events.  Nothing here is part of the library.
 //
 // Usage: mfma_peak [iterations]   (default 4000)
 
@@ -81,6 +83,21 @@ __global__ __launch_bounds__(256) void hbm_copy(const u32x4_t* __restrict__ src,
 __global__ __launch_bounds__(256) void hbm_write(u32x4_t* __restrict__ dst, size_t n) {
   const u32x4_t v = {1, 2, 3, 4};
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = v;
+}
+
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void lds_read(unsigned* out, int iters) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[65536];
+  for (int i = threadIdx.x; i < 65536 / 16; i += THREADS) reinterpret_cast<u32x4_t*>(lds)[i] = u32x4_t{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  const unsigned base = (unsigned)((threadIdx.x >> 6) * 4096 + (threadIdx.x & 63) * 16);
+  u32x4_t acc = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)  // every address in [0, 65536 - 16], 16-byte aligned
+      acc ^= *reinterpret_cast<const u32x4_t*>(lds + ((base + (unsigned)r * 1024u + (unsigned)(it & 3) * 16384u) & 0xFFF0u));
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9E3779B9u) out[0] = 1;  // keeps the reads alive
 }
 
 bool ok(hipError_t e, const char* what) {
@@ -183,6 +200,28 @@ int main(int argc, char** argv) {
   }
   (void)hipFree(a);
   (void)hipFree(b);
+
+  // LDS
+  const int lds_iters = 20000;
+  std::printf("LDS (16-byte reads, one workgroup per CU, %d x 16 reads per lane)\n", lds_iters);
+  for (int threads : {256, 512, 1024}) {
+    auto launch = [&] {
+      if (threads == 256) hipLaunchKernelGGL(lds_read<256>, dim3(blocks), dim3(256), 0, 0, flag, lds_iters);
+      if (threads == 512) hipLaunchKernelGGL(lds_read<512>, dim3(blocks), dim3(512), 0, 0, flag, lds_iters);
+      if (threads == 1024) hipLaunchKernelGGL(lds_read<1024>, dim3(blocks), dim3(1024), 0, 0, flag, lds_iters);
+    };
+    launch();
+    if (!ok(hipDeviceSynchronize(), "lds warm-up")) return 1;
+    (void)hipEventRecord(e0);
+    launch();
+    (void)hipEventRecord(e1);
+    if (!ok(hipEventSynchronize(e1), "lds run")) return 1;
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    const double bytes = (double)threads * 16.0 * 16.0 * lds_iters * blocks;
+    std::printf("%4d threads per CU %8.3f ms  %7.1f TB/s  %6.0f GB/s per CU\n", threads, ms, bytes / (ms * 1e-3) / 1e12,
+                bytes / blocks / (ms * 1e-3) / 1e9);
+  }
   (void)hipFree(flag);
   return 0;
 }

@@ -806,7 +806,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: wave-level addresses in scalar registers
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int l32 = lane & 31, h = lane >> 5;
   const int tiles_n = (N + T::BN - 1) / T::BN;
@@ -1054,31 +1054,29 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // Read a wave's operands of one K-step from its LDS stage: per fragment the scale register
 // (byte 0: block h, byte 1: block 2 + h of the lane's row) and the two instructions' code chunks.
+// Fragment and wave row offsets are multiples of 32, so a row's chunk swizzle depends on l32
+// alone: every read is a per-lane base plus an immediate.
 template <class T, class D>
 __device__ __forceinline__ void mx_read(const uint8_t* cur, int wm, int wn, int l32, int h, uint32_t psel,
                                         uint32_t (&sA)[T::FRAG_M], uint32_t (&sB)[T::FRAG_N],
                                         i32x4_t (&cA)[2][T::FRAG_M], i32x4_t (&cB)[2][T::FRAG_N]) {
+  const int sw4 = (l32 >> 2) & 3;
+  const int ra = wm * T::FRAG_M * 32 + l32, rb = T::BM + wn * T::FRAG_N * 32 + l32;  // the lane's first rows
 #pragma unroll
   for (int i = 0; i < T::FRAG_M; ++i) {
-    const int row = wm * T::FRAG_M * 32 + i * 32 + l32;
-    const int sw4 = code_swizzle(row);
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (ra >> 2) * 16 + i * 8 * 16);
     sA[i] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
-    }
+    for (int s2 = 0; s2 < 2; ++s2)
+      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + ra * 64 + 16 * ((2 * s2 + h) ^ sw4) + i * 32 * 64);
   }
 #pragma unroll
   for (int j = 0; j < T::FRAG_N; ++j) {
-    const int row = T::BM + wn * T::FRAG_N * 32 + j * 32 + l32;
-    const int sw4 = code_swizzle(row);
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (rb >> 2) * 16 + j * 8 * 16);
     sB[j] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
-    }
+    for (int s2 = 0; s2 < 2; ++s2)
+      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + rb * 64 + 16 * ((2 * s2 + h) ^ sw4) + j * 32 * 64);
   }
 }
 
@@ -1088,27 +1086,25 @@ template <class T, class D>
 __device__ __forceinline__ void mx_read_raw(const uint8_t* cur, int wm, int wn, int l32, int h,
                                             uint32_t (&qA)[T::FRAG_M][2], uint32_t (&qB)[T::FRAG_N][2],
                                             i32x4_t (&cA)[2][T::FRAG_M], i32x4_t (&cB)[2][T::FRAG_N]) {
+  const int sw4 = (l32 >> 2) & 3;
+  const int ra = wm * T::FRAG_M * 32 + l32, rb = T::BM + wn * T::FRAG_N * 32 + l32;
 #pragma unroll
   for (int i = 0; i < T::FRAG_M; ++i) {
-    const int row = wm * T::FRAG_M * 32 + i * 32 + l32;
-    const int sw4 = code_swizzle(row);
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (ra >> 2) * 16 + i * 8 * 16);
     qA[i][0] = sq[h];
     qA[i][1] = sq[2 + h];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
-      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
+      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + ra * 64 + 16 * ((2 * s2 + h) ^ sw4) + i * 32 * 64);
   }
 #pragma unroll
   for (int j = 0; j < T::FRAG_N; ++j) {
-    const int row = T::BM + wn * T::FRAG_N * 32 + j * 32 + l32;
-    const int sw4 = code_swizzle(row);
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (row >> 2) * 16);
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (rb >> 2) * 16 + j * 8 * 16);
     qB[j][0] = sq[h];
     qB[j][1] = sq[2 + h];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
-      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + row * 64 + 16 * ((2 * s2 + h) ^ sw4));
+      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + rb * 64 + 16 * ((2 * s2 + h) ^ sw4) + j * 32 * 64);
   }
 }
 
@@ -1185,7 +1181,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: wave-level addresses in scalar registers
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int l32 = lane & 31, h = lane >> 5;
   const int tiles_n = (N + T::BN - 1) / T::BN;

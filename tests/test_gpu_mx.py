@@ -106,6 +106,7 @@ def _check_gemm_mx(w4, lay, bias=False):
     if bias:  # one more float32 addition
         lim = lim + 2.0 ** -23 * (np.abs(b_f)[None, :] + np.abs(y_ref))
     assert np.all(err <= lim), f"per-element bound broken: worst excess {np.max(err - lim):.3e}"
+    return y_gpu
 
 
 @pytest.mark.parametrize("M,N,K,R", [(64, 256, 256, 32), (130, 200, 384, 8), (37, 68, 128, 0), (3, 40, 256, 64),

@@ -840,11 +840,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 // the first pass is staged and land while the epilogue computes.  y leaves through buffer
 // stores: a chunk outside y gets an offset the hardware drops, so every wave issues exactly ST
 // stores per tile (before the first tile, ST dropped ones), and each tile's first waits count
-// them in: the stores drain while K-steps 0 and 1 run on the matrix cores.  Needs whole 16-byte runs of y rows (N % 8 == 0, y
-// 16-byte aligned) and |y| below 2^31 bytes.
-template <class T>
+// them in: the stores drain while K-steps 0 and 1 run on the matrix cores.  Loads and stores
+// of a wave complete in issue order on this target (the compiler's own waits assume the same).
+// Needs whole 16-byte runs of y rows (N % 8 == 0, y 16-byte aligned) and |y| below 2^31 bytes.
+template <class T, class D = DmaTile<T>>
 struct PersistTile {
-  using D = DmaTile<T>;
   static constexpr int RW = 32;      // ranks staged per pass
   static constexpr int RS = RW + 8;  // rank stride of the staged operands: 80-byte rows put the 16-byte
                                      // reads of 16 consecutive rows on distinct banks
@@ -861,8 +861,124 @@ struct PersistTile {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
 
+// N buffer stores that the hardware drops (offsets from 2^31 up, past any y the persistent kernels
+// accept), each to its own offset so that none is merged with another.
+template <int N>
+__device__ __forceinline__ void drop_stores(__amdgpu_buffer_rsrc_t yr) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, yr, (int)(0x80000000u + 16u * (uint32_t)i), 0, 0);
+}
+
 // LDS-only barrier: waits for this wave's LDS operations, not for its loads or stores in flight.
 __device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Epilogue of one tile in the persistent kernels (as `epilogue`, whole-tile form): the operands are
+// staged in a region E after stage slots 0 and 1, 32 ranks per pass; `prefetch` runs once the first
+// pass is staged (it issues the next tile's first K-steps into slots 0 and 1); y leaves through
+// exactly P::ST buffer stores per wave, chunks outside y at an offset the hardware drops.
+template <class T, class P, bool LORA, class Prefetch>
+__device__ __forceinline__ void persist_epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N], uint8_t* lds, int wave, int lane,
+                                                 int m0, int n0, int M, int N, int R, int parts,
+                                                 const float* __restrict__ lora, const uint16_t* __restrict__ pu,
+                                                 const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts,
+                                                 const uint16_t* __restrict__ bias, __amdgpu_buffer_rsrc_t yr,
+                                                 Prefetch&& prefetch) {
+  constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
+  constexpr int rw = P::RW, rs = P::RS, RSB = P::RSB, CPR = P::CPR;
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int t = wave * 64 + lane;
+  const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank
+  uint8_t* const E = lds + P::E_OFF;
+  const uint16_t* l_hi = reinterpret_cast<const uint16_t*>(E);
+  const uint16_t* l_lo = l_hi + T::BM * rs;
+  const uint16_t* p_lds = l_lo + T::BM * rs;
+  const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
+  const float* b_lds = c_lds + T::BN;
+  // epilogue operands, first pass; then the caller's prefetch of the next tile
+  stage_epilogue<T, LORA>(E, rs, 0, min(rp, rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
+  prefetch();
+  lds_only_barrier();
+
+  // acc *= wcscales * wtscale; + L @ proj_up^T (passes of 32 ranks); + bias (as in `epilogue`)
+  const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
+    }
+  if (LORA) {
+    for (int lo = 0; lo < rp; lo += rw) {
+      if (lo > 0) {
+        lds_only_barrier();  // every wave is done with the previous pass
+        stage_epilogue<T, LORA>(E, rs, lo, min(rp, lo + rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
+        lds_only_barrier();
+      }
+      for (int r0 = 0; r0 < min(rp - lo, rw); r0 += 16) {
+        bf16x8_t pv[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          pv[j] = *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * rs + r0 + 8 * h);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = wm * FM * 32 + i * 32 + l32;
+          const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * rs + r0 + 8 * h);
+          const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], llo, acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  if (bias != nullptr) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4_t b = *reinterpret_cast<const float4_t*>(b_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] += b[e];
+      }
+  }
+  lds_only_barrier();  // every wave is done with the staged operands: E becomes store regions
+
+  // one fragment row at a time through the wave's region (chunk ch of region row r at
+  // (ch + r / 2) % CPR), then whole 16-byte runs of y rows
+  uint8_t* reg = E + wave * 32 * RSB;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = 4 * j + q;
+        const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        *reinterpret_cast<u32x2_t*>(reg + l32 * RSB + 16 * ((ch + (l32 >> 1)) % CPR) + 8 * h) = u32x2_t{p0, p1};
+      }
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < CPR / 2; ++it) {
+      const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR));
+      const int m = mb + i * 32 + r, n = nb + 8 * ch;
+      const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b128(val, yr, (int)off, 0, 0);
+    }
+    wave_lds_sync();  // the region is rewritten by the next fragment row
+  }
+}
 
 template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kernel(
@@ -874,7 +990,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
   using D = DmaTile<T>;
   using P = PersistTile<T>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[P::LDS_BYTES];
-  constexpr int rw = P::RW, rs = P::RS, RSB = P::RSB, CPR = P::CPR;
 
   const int lane0 = (int)threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform: wave-level addresses in scalar registers
@@ -883,15 +998,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
   const int tiles = tiles_m * tiles_n;
   const int nkt = K / BK;
   const uint32_t kbytes = (uint32_t)K / 2;
-  const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank
   const uint32_t ybytes = (uint32_t)M * (uint32_t)N * 2u;
   const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(y, 0, (int)ybytes, 0x00020000);
-  uint8_t* const E = lds + P::E_OFF;
-  const uint16_t* l_hi = reinterpret_cast<const uint16_t*>(E);
-  const uint16_t* l_lo = l_hi + T::BM * rs;
-  const uint16_t* p_lds = l_lo + T::BM * rs;
-  const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
-  const float* b_lds = c_lds + T::BN;
 
   int v = (int)blockIdx.x;
   int tm, tn;
@@ -902,17 +1010,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
     ad.issue(lds, wave, 0);
     ad.issue(lds + D::STAGE, wave, nkt > 1 ? 1 : 0);
   }
-  // ST stores the hardware drops (offset past y), so that the first tile's waits count the same
-  // stores as every later tile's: one copy of the K loop
-#pragma unroll
-  for (int i = 0; i < P::ST; ++i) __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, yr, (int)0x80000000u, 0, 0);
+  // ST stores the hardware drops (offsets past y), so that the first tile's waits count the same
+  // stores as every later tile's: one copy of the K loop.  Each has its own offset: identical
+  // stores to one address would be merged into one by the compiler.
+  drop_stores<P::ST>(yr);
   for (;;) {
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     // Lane-derived addresses are recomputed in each phase rather than hoisted out of the tile
     // loop, where the K loop's and the epilogue's would all stay live at once.
     int lane = lane0;
     asm volatile("" : "+v"(lane));
-    int l32 = lane & 31, h = lane >> 5;
+    const int l32 = lane & 31, h = lane >> 5;
     DmaAddr<T> ad;
     ad.set(wave, lane, m0, n0, M, N, kbytes, qa, sa, qw, sw);
     float16_t acc[FM][FN];
@@ -924,100 +1032,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     dma_k_loop<T, P::ST>(acc, lds, ad, wave, wm, wn, l32, h, nkt);
 
-    // epilogue operands, first pass; then the next tile's K-steps 0 and 1 into slots 0 and 1
+    // epilogue; once its first operand pass is staged, the next tile's K-steps 0 and 1 go into
+    // slots 0 and 1
     asm volatile("" : "+v"(lane));
-    l32 = lane & 31;
-    h = lane >> 5;
-    const int t = wave * 64 + lane;
-    stage_epilogue<T, LORA>(E, rs, 0, min(rp, rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
     const int vn = v + (int)gridDim.x;
     const bool more = vn < tiles;  // workgroup-uniform
-    if (more) {
-      tile_of(vn, tiles, tiles_m, tiles_n, tm, tn);
-      DmaAddr<T> nad;
-      nad.set(wave, lane, tm * T::BM, tn * T::BN, M, N, kbytes, qa, sa, qw, sw);
-      nad.issue(lds, wave, 0);
-      nad.issue(lds + D::STAGE, wave, nkt > 1 ? 1 : 0);
-    }
-    lds_only_barrier();
-
-    // acc *= wcscales * wtscale; + L @ proj_up^T (passes of 32 ranks); + bias (as in `epilogue`)
-    const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
+    persist_epilogue<T, P, LORA>(acc, lds, wave, lane, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, yr, [&] {
+      if (more) {
+        tile_of(vn, tiles, tiles_m, tiles_n, tm, tn);
+        DmaAddr<T> nad;
+        nad.set(wave, lane, tm * T::BM, tn * T::BN, M, N, kbytes, qa, sa, qw, sw);
+        nad.issue(lds, wave, 0);
+        nad.issue(lds + D::STAGE, wave, nkt > 1 ? 1 : 0);
       }
-    if (LORA) {
-      for (int lo = 0; lo < rp; lo += rw) {
-        if (lo > 0) {
-          lds_only_barrier();  // every wave is done with the previous pass
-          stage_epilogue<T, LORA>(E, rs, lo, min(rp, lo + rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
-          lds_only_barrier();
-        }
-        for (int r0 = 0; r0 < min(rp - lo, rw); r0 += 16) {
-          bf16x8_t pv[FN];
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            pv[j] = *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * rs + r0 + 8 * h);
-#pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int row = wm * FM * 32 + i * 32 + l32;
-            const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * rs + r0 + 8 * h);
-            const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], llo, acc[i][j], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
-    if (bias != nullptr) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4_t b = *reinterpret_cast<const float4_t*>(b_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] += b[e];
-        }
-    }
-    lds_only_barrier();  // every wave is done with the staged operands: E becomes store regions
-
-    // one fragment row at a time through the wave's region (chunk ch of region row r at
-    // (ch + r / 2) % CPR), then whole 16-byte runs of y rows
-    uint8_t* reg = E + wave * 32 * RSB;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ch = 4 * j + q;
-          const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-          const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<u32x2_t*>(reg + l32 * RSB + 16 * ((ch + (l32 >> 1)) % CPR) + 8 * h) = u32x2_t{p0, p1};
-        }
-      wave_lds_sync();
-#pragma unroll
-      for (int it = 0; it < CPR / 2; ++it) {
-        const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
-        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR));
-        const int m = mb + i * 32 + r, n = nb + 8 * ch;
-        const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b128(val, yr, (int)off, 0, 0);
-      }
-      wave_lds_sync();  // the region is rewritten by the next fragment row
-    }
+    });
     if (!more) break;
     v = vn;
   }

@@ -206,6 +206,33 @@ def test_gemm_persistent_tile_walk(w4, variant, grid, R, bias, monkeypatch):
     assert np.array_equal(y_gpu, y_one), "persistent and one-tile-per-workgroup outputs differ"
 
 
+@pytest.mark.parametrize("M,N", [(32764, 32768), (32772, 32776)])
+def test_gemm_output_around_2gib(w4, M, N):
+    """y of about 2 GiB: just below 2^31 bytes the persistent kernel runs (32-bit buffer offsets up
+    to the last chunk), just above it the one-tile-per-workgroup kernel (64-bit row offsets, ragged
+    last tiles).  Checked against the oracle on sampled rows and columns, the last ones included."""
+    import torch
+    K, R = 128, 16
+    lay = synth.make_layer("tiny", seed=M % 97, M=M, K=K, N=N, R=R, B=0, wcs="uniform")
+    f = synth.as_f32(lay)
+    qw, ws = H.oracle_weights(lay)
+    qa, sa, lo = oquant.quantize_act(f["x"], f["smooth_factor"], f["proj_down"], lay["B"])
+    lo32 = lo.astype(np.float32)
+    y = w4.svdq_gemm_lowrank(H.to_dev_u8(qa), H.to_dev_u8(sa), torch.from_numpy(lo32).cuda(), H.to_dev_u8(qw),
+                             H.to_dev_u8(ws), H.to_dev_bf16(lay["proj_up"]), H.to_dev_bf16(lay["wcscales"]),
+                             H.to_dev_bf16(lay["wtscale"]))
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, M - 1, M - 2], rng.choice(M, 61, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1, N - 8], rng.choice(N, 125, replace=False)]))
+    ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    y_s = y.index_select(0, ri).index_select(1, ci)
+    torch.cuda.synchronize()
+    del y
+    _, y_ref = olinear.gemm_lowrank(qa[rows], sa[:, rows], lo32[rows], qw[cols], ws[:, cols], f["proj_up"][cols],
+                                    f["wcscales"][cols], f["wtscale"])
+    H.assert_gates(H.from_dev_bf16_f64(y_s), y_ref, f"gemm y of {M * N * 2} bytes")
+
+
 @pytest.mark.parametrize("M,N,K,R,B", [(64, 256, 256, 32, 0), (37, 70, 256, 32, 128), (3, 40, 48, 3, 16),
                                        (150, 260, 512, 64, 64),
                                        # small batches: K split across quantizer workgroups (partial low-rank sums)

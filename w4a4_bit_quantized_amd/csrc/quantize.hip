@@ -55,7 +55,10 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int max_waves(int hb, int rb) { return (rb > 2 || (hb == 128 && rb > 0)) ? 8 : 16; }
+// Waves per workgroup, set by the register budget of the variant: 16 (four per SIMD) where a wave
+// needs at most 128 VGPRs; 12 (three per SIMD) for the 128-point rotation with rank <= 32 (140-145
+// VGPRs: twelve waves hide more latency than eight, sixteen would spill); 8 above rank 32.
+constexpr int max_waves(int hb, int rb) { return rb > 2 ? 8 : (hb == 128 && rb > 0) ? 12 : 16; }
 
 template <int HB, bool ACT, int RB>
 struct QCfg {

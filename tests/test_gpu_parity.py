@@ -206,6 +206,40 @@ def test_gemm_persistent_tile_walk(w4, variant, grid, R, bias, monkeypatch):
     assert np.array_equal(y_gpu, y_one), "persistent and one-tile-per-workgroup outputs differ"
 
 
+@pytest.mark.parametrize("M,K,N,R,B", [(600, 1024, 1040, 32, 64), (16, 2048, 8200, 32, 0)])
+def test_linear_in_hip_graph(w4, M, K, N, R, B):
+    """svdq_linear (quantizer + persistent GEMM with bias; and the skinny path with K-split
+    partial sums) captured once in a HIP graph and replayed four times, with eager launches of
+    the same kernels on other inputs between the replays: every replay is bit-identical to the
+    eager call."""
+    import torch
+    lay = synth.make_layer("tiny", seed=M + N, M=M, K=K, N=N, R=R, B=B, wcs="uniform")
+    qw, ws = H.oracle_weights(lay)
+    layer = H.device_layer(lay, qw, ws)
+    layer["bias"] = H.to_dev_bf16(H.seeded_bias(N, M))
+    x = H.to_dev_bf16(lay["x"])
+    x_other = H.to_dev_bf16(synth.make_layer("tiny", seed=M + N + 1, M=M, K=K, N=N, R=R, B=B, wcs="uniform")["x"])
+    ref = w4.svdq_linear(x, layer, hadamard_block=B)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w4.svdq_linear(x, layer, hadamard_block=B)
+        with torch.cuda.graph(g, stream=s):
+            y_g = w4.svdq_linear(x, layer, hadamard_block=B)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y_g.zero_()
+        other = w4.svdq_linear(x_other, layer, hadamard_block=B)  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, ref), f"replay {rep} differs from the eager result"
+        assert not torch.equal(other, ref)
+
+
 @pytest.mark.parametrize("M,N", [(32764, 32768), (32772, 32776)])
 def test_gemm_output_around_2gib(w4, M, N):
     """y of about 2 GiB: just below 2^31 bytes the persistent kernel runs (32-bit buffer offsets up

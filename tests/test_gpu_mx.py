@@ -233,3 +233,33 @@ def test_quantize_act_mx_special_values(w4, B):
     assert np.array_equal(sa.cpu().numpy(), s_ref)
     assert np.array_equal(qa.cpu().numpy(), q_ref)
     assert s_ref[0, 0] == 0 and s_ref[0, 2] == 127 + 3 and s_ref[0, 4] == 127 + 4 if B == 0 else True
+
+
+def test_linear_mx_in_hip_graph(w4):
+    """svdq_linear_mx captured once in a HIP graph and replayed four times, with eager launches on
+    another input between the replays: every replay is bit-identical to the eager call."""
+    import torch
+    lay = _lay(600, 1024, 1040, 32, 32, seed=77)
+    qw, sw = _mx_weights(lay)
+    layer = H.device_layer(lay, qw, sw)
+    x = H.to_dev_bf16(lay["x"])
+    x_other = H.to_dev_bf16(_lay(600, 1024, 1040, 32, 32, seed=78)["x"])
+    ref = w4.svdq_linear_mx(x, layer, hadamard_block=32)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w4.svdq_linear_mx(x, layer, hadamard_block=32)
+        with torch.cuda.graph(g, stream=s):
+            y_g = w4.svdq_linear_mx(x, layer, hadamard_block=32)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y_g.zero_()
+        other = w4.svdq_linear_mx(x_other, layer, hadamard_block=32)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, ref), f"replay {rep} differs from the eager result"
+        assert not torch.equal(other, ref)

@@ -11,27 +11,30 @@
 // (4 significant bits) per 16: neither the granularity nor the mantissa fits.
 // Each dequantized operand e2m1 * e4m3 has at most 6 significant bits and
 // lies in [2^-10, 2688], so it is exact in f16, and every product is exact in
-// the f32 accumulator.  The kernel stages the packed codes and the scales
-// (converted once to f16 while staging) through LDS, decodes in registers
-// with the hardware E2M1->f16 convert plus one packed f16 multiply, and issues
+// the f32 accumulator.  The kernels stage the packed codes and the e4m3 scales
+// through LDS, widen each scale pair to f16 and decode in registers with the
+// hardware E2M1->f16 convert plus one packed f16 multiply, and issue
 // v_mfma_f32_32x32x16_f16.  Only the f32 accumulation order differs from the
 // exact sum.
 //
-// Tiling: a workgroup of WAVES_M x WAVES_N waves computes a BM x BN tile; a
-// wave owns FM x FN blocks of 32 x 32.  K advances 128 columns (8 groups) per
-// LDS stage, double-buffered.  Within a stage, lane half h (lane / 32) owns
-// K-columns [64h, 64h + 64); MFMA sub-step kk feeds columns 64h + 8kk .. +8
-// into the instruction's k-slots 8h .. 8h+8.  A and W use the same mapping,
-// so the contraction covers every column exactly once.  The decode work per
-// MFMA is (FM + FN) / (FM * FN) eight-element decodes, which is why the large
-// tiles (4 x 4 and 4 x 3 blocks per wave) are used for the DiT shapes.
+// Tiling: a workgroup of WAVES_M x WAVES_N waves computes a BM x BN tile; a wave owns FM x FN
+// blocks of 32 x 32.  K advances 128 columns (8 groups) per LDS stage.  The main kernels load
+// each K-step straight into LDS (global_load_lds, three stages, K-step kt + 2 in flight while
+// kt is computed); other shapes use a register-staged two-stage pipeline.  Within a stage,
+// lane half h (lane / 32) owns K-columns [64h, 64h + 64); MFMA sub-step kk feeds columns
+// 64h + 8kk .. +8 into the instruction's k-slots 8h .. 8h+8.  A and W use the same mapping,
+// so the contraction covers every column exactly once.  The decode work per MFMA is
+// (FM + FN) / (FM * FN) eight-element decodes, which is why the large tiles (4 x 2 and 2 x 3
+// blocks per wave, 8 waves) are used for the DiT shapes.
 //
-// Epilogue: acc *= wcscales[n] * wtscale; the rank-R correction is
-// accumulated on the matrix cores (bf16 32x32x16, L split into bf16 hi + lo
-// parts, proj_up exact in bf16); each lane rounds its values to bf16 (nearest
-// even) and stores 4 consecutive n of one m as one 8-byte write.  The epilogue
-// operands of the tile (L summed over its partial sums and split into bf16 hi +
-// lo, proj_up, wcscales * wtscale) are first staged in LDS with coalesced loads.
+// Epilogue: acc *= wcscales * wtscale; the rank-R correction is accumulated on the matrix
+// cores (bf16 32x32x16, L split into bf16 hi + lo parts, proj_up exact in bf16); values are
+// rounded to bf16 (nearest even) and, when y rows are whole 16-byte runs, pass through a
+// per-wave LDS region so that each lane stores 16 contiguous bytes.  The epilogue operands of
+// the tile (L summed over its partial sums, proj_up, wcscales * wtscale, bias) are first
+// staged in LDS with coalesced loads.  By default the direct-load kernel is persistent: one
+// workgroup per CU walks its tiles and fetches the next tile's first K-steps during the
+// epilogue (gemm_dma_persist_kernel).
 #include <cstdlib>
 #include <cstring>
 

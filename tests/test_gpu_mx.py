@@ -117,19 +117,19 @@ def test_gemm_lowrank_mx_parity(w4, M, N, K, R):
 
 @pytest.mark.parametrize("tile", ["4x4x2x2", "2x4x4x2", "2x2x2x2", "2x2x4x4"])
 @pytest.mark.parametrize("N", [520, 516])
-def test_gemm_mx_each_tile(w4, tile, N, monkeypatch):
+def test_gemm_mx_each_tile(w4, tile, N, hooks):
     """Each MX tile layout (2x2x4x4: one wave per SIMD with register prefetch)
     on a ragged shape with an odd number of K-steps, with y rows that are whole 16-byte runs
     (N = 520) and that are not (N = 516)."""
-    monkeypatch.setenv("W4A4_GEMM_TILE", tile)
+    hooks.setenv("W4A4_GEMM_TILE", tile)
     _check_gemm_mx(w4, _lay(300, 640, N, 32, 0, seed=41))
 
 
 @pytest.mark.parametrize("tile", ["4x4x2x2", "2x2x4x4"])
 @pytest.mark.parametrize("K", [128, 256, 384])
-def test_gemm_mx_few_k_steps(w4, tile, K, monkeypatch):
+def test_gemm_mx_few_k_steps(w4, tile, K, hooks):
     """Fewer K-steps than pipeline stages."""
-    monkeypatch.setenv("W4A4_GEMM_TILE", tile)
+    hooks.setenv("W4A4_GEMM_TILE", tile)
     _check_gemm_mx(w4, _lay(260, K, 264, 16, 0, seed=K))
 
 
@@ -148,37 +148,10 @@ def test_linear_mx_parity(w4, M, N, K, R, B):
     H.assert_gates(H.from_dev_bf16_f64(y), y_ref, "svdq_linear_mx")
 
 
-def test_linear_mx_full_size_dit_mlp_up(w4):
-    """The DiT MLP up-projection shape (M=4096, K=3072, N=12288, R=32) through the MX layer with a
-    group-32 rotation, checked on sampled rows and columns."""
-    import torch
-    lay = synth.make_layer("dit_mlp_up", seed=0)
-    M, N, K = lay["M"], lay["N"], lay["K"]
-    rng = np.random.default_rng(321)
-    rows = np.sort(rng.choice(M, 32, replace=False))
-    cols = np.sort(rng.choice(N, 192, replace=False))
-    qw_d, sw_d = w4.svdq_quantize_weight_mx(H.to_dev_bf16(lay["w"]), H.to_dev_bf16(lay["smooth_factor"]), 32)
-    f = synth.as_f32(lay)
-    qw_ref, sw_ref = omx.quantize_weight_mx(f["w"][cols], f["smooth_factor"], 32)
-    torch.cuda.synchronize()
-    assert np.array_equal(qw_d.cpu().numpy()[cols], qw_ref)
-    assert np.array_equal(sw_d.cpu().numpy()[:, cols], sw_ref)
-    layer = H.device_layer(lay, np.zeros((1, 1), np.uint8), np.zeros((1, 1), np.uint8))
-    layer["qweight"], layer["wscales"] = qw_d, sw_d
-    y = w4.svdq_linear_mx(H.to_dev_bf16(lay["x"]), layer, hadamard_block=32)
-    torch.cuda.synchronize()
-    y_gpu = H.from_dev_bf16_f64(y)[np.ix_(rows, cols)]
-    sub = dict(qweight=qw_ref, wscales=sw_ref, proj_down=f["proj_down"], proj_up=f["proj_up"][cols],
-               smooth_factor=f["smooth_factor"], wcscales=f["wcscales"][cols], wtscale=f["wtscale"])
-    _, y_ref, _ = omx.svdq_linear_mx(f["x"][rows], sub, 32)
-    rel, mx = H.assert_gates(y_gpu, y_ref, "dit_mlp_up mx")
-    print(f"\ndit_mlp_up mx: parity rel_fro={rel:.2e} max={mx:.2e}")
-
-
 @pytest.mark.parametrize("tile", ["4x4x2x2", "2x2x4x4", "2x2x2x2"])
-def test_gemm_mx_bias(w4, tile, monkeypatch):
+def test_gemm_mx_bias(w4, tile, hooks):
     """The optional bias (rotate notes, section 3.2) through the MX GEMM's bias entry point."""
-    monkeypatch.setenv("W4A4_GEMM_TILE", tile)
+    hooks.setenv("W4A4_GEMM_TILE", tile)
     _check_gemm_mx(w4, _lay(300, 640, 520, 32, 0, seed=43), bias=True)
 
 

@@ -151,10 +151,10 @@ def test_gemm_lowrank_parity(w4, M, N, K, R):
 @pytest.mark.parametrize("path", ["wide", "stream", "regs"])
 @pytest.mark.parametrize("M,N,K,R", [(16, 600, 5120, 32), (1, 64, 512, 8), (13, 36, 8192, 64), (16, 100, 1024, 0),
                                      (8, 200, 2560, 16), (12, 68, 3584, 32), (4, 40, 512, 64), (16, 130, 1024, 33)])
-def test_skinny_paths(w4, M, N, K, R, path, monkeypatch):
+def test_skinny_paths(w4, M, N, K, R, path, hooks):
     """Each weight-streaming kernel (64-row wide, 32-row LDS-staged, registers-only), forced
     through W4A4_SKINNY_PATH; shapes a variant does not accept fall back to the next one."""
-    monkeypatch.setenv("W4A4_SKINNY_PATH", path)
+    hooks.setenv("W4A4_SKINNY_PATH", path)
     lay = synth.make_layer("tiny", seed=M * 3 + K, M=M, K=K, N=N, R=R, B=0, wcs="uniform")
     _check_gemm(w4, lay)
 
@@ -164,22 +164,22 @@ GEMM_VARIANTS = ["2x2x4x4", "2x2x4x3", "2x2x4x2", "2x2x2x2", "4x2x2x4", "2x4x4x2
 
 @pytest.mark.parametrize("path", ["dma", "stage"])
 @pytest.mark.parametrize("variant", GEMM_VARIANTS)
-def test_gemm_every_tile_variant(w4, variant, path, monkeypatch):
+def test_gemm_every_tile_variant(w4, variant, path, hooks):
     """Each compiled tile layout of both K pipelines (direct LDS loads, and register staging forced
     through W4A4_GEMM_PATH), forced through W4A4_GEMM_TILE, on a shape with ragged edges."""
-    monkeypatch.setenv("W4A4_GEMM_TILE", variant)
-    monkeypatch.setenv("W4A4_GEMM_PATH", path)
+    hooks.setenv("W4A4_GEMM_TILE", variant)
+    hooks.setenv("W4A4_GEMM_PATH", path)
     lay = synth.make_layer("tiny", seed=31, M=300, K=640, N=520, R=32, B=0, wcs="uniform")
     _check_gemm(w4, lay)
 
 
 @pytest.mark.parametrize("variant,path,N", [("2x2x4x4", "dma", 516), ("2x2x4x4", "stage", 518),
                                             ("2x4x4x2", "stage", 518), ("2x2x2x2", "dma", 516)])
-def test_gemm_tile_unaligned_rows(w4, variant, path, N, monkeypatch):
+def test_gemm_tile_unaligned_rows(w4, variant, path, N, hooks):
     """y rows that are not whole 16-byte runs leave the epilogue by direct stores (8-byte runs for
     N % 4 == 0, single values otherwise), in both the fragment-row-wise and the whole-tile epilogue."""
-    monkeypatch.setenv("W4A4_GEMM_TILE", variant)
-    monkeypatch.setenv("W4A4_GEMM_PATH", path)
+    hooks.setenv("W4A4_GEMM_TILE", variant)
+    hooks.setenv("W4A4_GEMM_PATH", path)
     lay = synth.make_layer("tiny", seed=N, M=300, K=640, N=N, R=32, B=0, wcs="uniform")
     _check_gemm(w4, lay)
 
@@ -188,19 +188,19 @@ def test_gemm_tile_unaligned_rows(w4, variant, path, N, monkeypatch):
                                                   ("4x2x2x3", 8, 5, True), ("4x2x2x3", 2, 0, False),
                                                   ("2x2x2x2", 5, 64, False), ("2x2x4x2", 4, 33, True),
                                                   ("2x2x4x3", 7, 16, False), ("4x2x2x4", 6, 32, True)])
-def test_gemm_persistent_tile_walk(w4, variant, grid, R, bias, monkeypatch):
+def test_gemm_persistent_tile_walk(w4, variant, grid, R, bias, hooks):
     """The persistent form of the direct-load kernel with the grid capped (W4A4_GEMM_GRID), so each
     workgroup walks several tiles of a ragged shape: the next tile's first K-steps load during the
     epilogue, ranks above 32 are staged in two passes, and out-of-range chunks are dropped by the
     buffer stores.  Checked against the oracle and bit for bit against one workgroup per tile
     (W4A4_GEMM_PERSIST=0)."""
     import torch
-    monkeypatch.setenv("W4A4_GEMM_TILE", variant)
-    monkeypatch.setenv("W4A4_GEMM_PATH", "dma")
-    monkeypatch.setenv("W4A4_GEMM_GRID", str(grid))
+    hooks.setenv("W4A4_GEMM_TILE", variant)
+    hooks.setenv("W4A4_GEMM_PATH", "dma")
+    hooks.setenv("W4A4_GEMM_GRID", str(grid))
     lay = synth.make_layer("tiny", seed=grid * 7 + R, M=300, K=640, N=520, R=R, B=0, wcs="uniform")
     y_gpu, _ = _check_gemm(w4, lay, bias=bias)
-    monkeypatch.setenv("W4A4_GEMM_PERSIST", "0")
+    hooks.setenv("W4A4_GEMM_PERSIST", "0")
     y_one, _ = _check_gemm(w4, lay, bias=bias)
     torch.cuda.synchronize()
     assert np.array_equal(y_gpu, y_one), "persistent and one-tile-per-workgroup outputs differ"
@@ -282,41 +282,6 @@ def test_linear_parity(w4, M, N, K, R, B):
     H.assert_gates(H.from_dev_bf16_f64(y), y_ref, "svdq_linear")
 
 
-@pytest.mark.parametrize("name", synth.ORDER)
-def test_workload_full_size(w4, name):
-    """Full-size run of each workload; outputs checked on sampled rows and columns."""
-    import torch
-    lay = synth.make_layer(name, seed=0)
-    M, N, K, B = lay["M"], lay["N"], lay["K"], lay["B"]
-    rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(M, min(M, 48), replace=False))
-    cols = np.sort(rng.choice(N, min(N, 256), replace=False))
-    # weights quantized on the GPU at full size, checked bit-exact on the sampled rows
-    qw_d, ws_d = w4.svdq_quantize_weight(H.to_dev_bf16(lay["w"]), H.to_dev_bf16(lay["smooth_factor"]), B)
-    f = synth.as_f32(lay)
-    qw_ref, ws_ref = oquant.quantize_weight(f["w"][cols], f["smooth_factor"], B)
-    torch.cuda.synchronize()
-    assert np.array_equal(qw_d.cpu().numpy()[cols], qw_ref)
-    assert np.array_equal(ws_d.cpu().numpy()[:, cols], ws_ref)
-    # activation quantizer at full size, checked bit-exact on sampled rows
-    _check_quant_act(w4, lay, rows)
-    # whole layer at full size
-    layer = H.device_layer(lay, np.zeros((1, 1), np.uint8), np.zeros((1, 1), np.uint8))
-    layer["qweight"], layer["wscales"] = qw_d, ws_d
-    y = w4.svdq_linear(H.to_dev_bf16(lay["x"]), layer, hadamard_block=B)
-    torch.cuda.synchronize()
-    y_gpu = H.from_dev_bf16_f64(y)[np.ix_(rows, cols)]
-    sub = dict(lay, x=lay["x"][rows], w=lay["w"][cols], proj_up=lay["proj_up"][cols], wcscales=lay["wcscales"][cols],
-               M=len(rows), N=len(cols))
-    _, y_ref, _ = H.oracle_linear_rows(sub, qw_ref, ws_ref)
-    rel, mx = H.assert_gates(y_gpu, y_ref, name)
-    ref_unq = olinear.unquantized_reference(f["x"][rows], f["w"][cols], f["proj_down"], f["proj_up"][cols],
-                                            f["smooth_factor"], f["wcscales"][cols], f["wtscale"])
-    rel_unq = np.linalg.norm(y_gpu - ref_unq) / np.linalg.norm(ref_unq)
-    print(f"\n{name}: parity rel_fro={rel:.2e} max={mx:.2e}; vs unquantized linear (reported, not gated) "
-          f"rel_fro={rel_unq:.3f}")
-
-
 def test_empty_batch(w4):
     import torch
     lay = synth.make_layer("tiny", seed=1, M=4, K=64, N=8, R=4)
@@ -386,15 +351,15 @@ def test_error_status_through_binding(w4):
 @pytest.mark.parametrize("variant,path,skinny", [(None, None, None), ("2x2x4x4", "dma", None),
                                                  ("2x2x2x2", "stage", None), (None, None, "wide"),
                                                  (None, None, "stream"), (None, None, "regs")])
-def test_gemm_bias(w4, variant, path, skinny, monkeypatch):
+def test_gemm_bias(w4, variant, path, skinny, hooks):
     """The bias entry point on every epilogue: the default tile, the fragment-row-wise tile, the
     register-staged kernel and the three skinny variants."""
     if variant:
-        monkeypatch.setenv("W4A4_GEMM_TILE", variant)
+        hooks.setenv("W4A4_GEMM_TILE", variant)
     if path:
-        monkeypatch.setenv("W4A4_GEMM_PATH", path)
+        hooks.setenv("W4A4_GEMM_PATH", path)
     if skinny:
-        monkeypatch.setenv("W4A4_SKINNY_PATH", skinny)
+        hooks.setenv("W4A4_SKINNY_PATH", skinny)
         lay = synth.make_layer("tiny", seed=17, M=16, K=1024, N=8200 if skinny == "wide" else 520, R=32, B=0,
                                wcs="uniform")
     else:
@@ -488,3 +453,29 @@ def test_w4a4_linear_from_state_dict(w4):
     torch.cuda.synchronize()
     assert tuple(y.shape) == (3, 16, 192)
     assert torch.equal(y, y2)
+
+
+def test_product_library_ignores_path_hooks(w4, monkeypatch):
+    """The product library has no test hooks: with every path-forcing variable set, the product
+    build still takes its automatic choice (bit-identical outputs), while the test build obeys."""
+    import torch
+    from conftest import _test_lib
+    from w4a4_bit_quantized_amd import binding
+    for M, N, K in [(300, 520, 640), (16, 600, 1024)]:
+        lay = synth.make_layer("tiny", seed=M, M=M, K=K, N=N, R=32, B=0, wcs="uniform")
+        qw, ws = H.oracle_weights(lay)
+        layer = H.device_layer(lay, qw, ws)
+        x = H.to_dev_bf16(lay["x"])
+        ref = w4.svdq_linear(x, layer).clone()
+        for k, v in (("W4A4_GEMM_TILE", "2x2x4x4"), ("W4A4_GEMM_PATH", "stage"), ("W4A4_GEMM_PERSIST", "0"),
+                     ("W4A4_GEMM_GRID", "3"), ("W4A4_SKINNY_PATH", "regs")):
+            monkeypatch.setenv(k, v)
+        assert binding._LIB is w4.load_library()
+        y = w4.svdq_linear(x, layer)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"product library changed its path under the hooks (M={M})"
+        monkeypatch.setattr(binding, "_LIB", _test_lib())
+        y_t = w4.svdq_linear(x, layer)  # the test build honours them: a different kernel, same gates
+        torch.cuda.synchronize()
+        H.assert_gates(H.from_dev_bf16_f64(y_t), H.from_dev_bf16_f64(ref), "forced path")
+        monkeypatch.undo()

@@ -69,19 +69,28 @@ def library_path():
     return os.environ.get("W4A4_LIBRARY", os.path.join(_HERE, "libw4a4.so"))
 
 
+def test_library_path():
+    """The test build (path-forcing hooks read from the environment); only tests load it."""
+    return os.path.join(_HERE, "libw4a4_test.so")
+
+
+def open_library(path):
+    """Open one build of the library and declare its C signatures (no caching)."""
+    if not os.path.exists(path):
+        raise W4A4Error(f"{os.path.basename(path)} is not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
 def load_library():
     """Load libw4a4.so (once) and declare its C signatures."""
     global _LIB
     if _LIB is None:
-        path = library_path()
-        if not os.path.exists(path):
-            raise W4A4Error(f"libw4a4.so is not built ({path}); run __graft_entry__.build()")
-        lib = ctypes.CDLL(path)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _LIB = lib
+        _LIB = open_library(library_path())
     return _LIB
 
 
@@ -121,6 +130,74 @@ def _dev(t, name, dtypes, device=None):
     return t
 
 
+def _shape(t, name, shape):
+    """Raise ValueError unless tensor ``t`` has exactly ``shape`` (the C ABI sees raw pointers, so
+    a mis-sized tensor would be read or written past its end)."""
+    got = tuple(int(d) for d in t.shape)
+    want = tuple(int(d) for d in shape)
+    if got != want:
+        raise ValueError(f"{name} has shape {got}, expected {want}")
+
+
+def check_quantize_act_shapes(x, smooth_factor, proj_down):
+    """Sizes (M, K, R) of an activation quantizer call, after checking that every tensor agrees."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D (M, K), got shape {tuple(x.shape)}")
+    M, K = (int(d) for d in x.shape)
+    if proj_down.dim() != 2:
+        raise ValueError(f"proj_down must be 2-D (K, R), got shape {tuple(proj_down.shape)}")
+    R = int(proj_down.shape[1])
+    _shape(smooth_factor, "smooth_factor", (K,))
+    _shape(proj_down, "proj_down", (K, R))
+    return M, K, R
+
+
+def check_gemm_shapes(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, y=None, bias=None,
+                      group=16, scale_rows=None):
+    """Sizes (M, N, K, R) of a GEMM call, after checking every tensor against them.  ``group`` is
+    16 (e4m3 scales) or 32 (E8M0); ``scale_rows`` the activation scale row count (default M)."""
+    for t, n in ((qact, "qact"), (qweight, "qweight"), (proj_up, "proj_up")):
+        if t.dim() != 2:
+            raise ValueError(f"{n} must be 2-D, got shape {tuple(t.shape)}")
+    M, K = int(qact.shape[0]), 2 * int(qact.shape[1])
+    N, R = int(qweight.shape[0]), int(proj_up.shape[1])
+    _shape(ascales, "ascales", (K // group, M if scale_rows is None else scale_rows))
+    _shape(lora_act, "lora_act", (M, R))
+    _shape(qweight, "qweight", (N, K // 2))
+    _shape(wscales, "wscales", (K // group, N))
+    _shape(proj_up, "proj_up", (N, R))
+    _shape(wcscales, "wcscales", (N,))
+    if wtscale.numel() != 1:
+        raise ValueError(f"wtscale must hold one value, got shape {tuple(wtscale.shape)}")
+    if y is not None:
+        _shape(y, "out", (M, N))
+    if bias is not None:
+        _shape(bias, "bias", (N,))
+    return M, N, K, R
+
+
+def check_layer_shapes(M, K, layer, group=16, y=None):
+    """Sizes (N, R) of a whole-layer call on an (M, K) input, after checking every checkpoint
+    tensor of ``layer`` (and ``out``, ``bias``) against them."""
+    qw, pu = layer["qweight"], layer["proj_up"]
+    if qw.dim() != 2 or pu.dim() != 2:
+        raise ValueError("qweight and proj_up must be 2-D")
+    N, R = int(qw.shape[0]), int(pu.shape[1])
+    _shape(qw, "qweight", (N, K // 2))
+    _shape(layer["wscales"], "wscales", (K // group, N))
+    _shape(layer["proj_down"], "proj_down", (K, R))
+    _shape(pu, "proj_up", (N, R))
+    _shape(layer["smooth_factor"], "smooth_factor", (K,))
+    _shape(layer["wcscales"], "wcscales", (N,))
+    if layer["wtscale"].numel() != 1:
+        raise ValueError(f"wtscale must hold one value, got shape {tuple(layer['wtscale'].shape)}")
+    if layer.get("bias") is not None:
+        _shape(layer["bias"], "bias", (N,))
+    if y is not None:
+        _shape(y, "out", (M, N))
+    return N, R
+
+
 def _bytes_dtypes():
     torch = _torch()
     return (torch.uint8, torch.int8)
@@ -144,7 +221,7 @@ def svdq_quantize_act(x, smooth_factor, proj_down, hadamard_block=0):
     M, K = x.shape
     _dev(smooth_factor, "smooth_factor", (torch.bfloat16,), dev)
     _dev(proj_down, "proj_down", (torch.bfloat16,), dev)
-    R = proj_down.shape[1]
+    M, K, R = check_quantize_act_shapes(x, smooth_factor, proj_down)
     qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     ascales = torch.empty((K // 16, M), dtype=torch.uint8, device=dev)
     lora = torch.empty((M, R), dtype=torch.float32, device=dev)
@@ -162,6 +239,7 @@ def svdq_quantize_weight(w, smooth_factor, hadamard_block=0):
     dev = w.device
     N, K = w.shape
     _dev(smooth_factor, "smooth_factor", (torch.bfloat16,), dev)
+    _shape(smooth_factor, "smooth_factor", (K,))
     qweight = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
     wscales = torch.empty((K // 16, N), dtype=torch.uint8, device=dev)
     st = lib.svdq_quantize_weight(_ptr(w), _ptr(smooth_factor), N, K, int(hadamard_block),
@@ -183,9 +261,9 @@ def svdq_gemm_lowrank(qact, ascales, lora_act, qweight, wscales, proj_up, wcscal
     _dev(proj_up, "proj_up", (torch.bfloat16,), dev)
     _dev(wcscales, "wcscales", (torch.bfloat16,), dev)
     _dev(wtscale, "wtscale", (torch.bfloat16,), dev)
-    M, K = qact.shape[0], qact.shape[1] * 2
-    N = qweight.shape[0]
-    R = proj_up.shape[1]
+    if bias is not None:
+        _dev(bias, "bias", (torch.bfloat16,), dev)
+    M, N, K, R = check_gemm_shapes(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, out, bias)
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _dev(y, "y", (torch.bfloat16,), dev)
     if bias is None:
@@ -223,12 +301,15 @@ def svdq_linear(x, layer, hadamard_block=0, workspace=None, out=None):
     _dev(t["wscales"], "wscales", _scale_dtypes(), dev)
     for k in ("proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale"):
         _dev(t[k], k, (torch.bfloat16,), dev)
-    N = t["qweight"].shape[0]
-    R = t["proj_up"].shape[1]
+    if layer.get("bias") is not None:
+        _dev(layer["bias"], "bias", (torch.bfloat16,), dev)
+    N, R = check_layer_shapes(M, K, layer, group=16, y=out)
     need = int(lib.svdq_linear_workspace_bytes(M, K, R))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _dev(workspace, "workspace", (torch.uint8,), dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _dev(y, "y", (torch.bfloat16,), dev)
     common = (_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]), _ptr(t["proj_up"]),
@@ -264,7 +345,7 @@ def svdq_quantize_act_mx(x, smooth_factor, proj_down, hadamard_block=32):
     M, K = x.shape
     _dev(smooth_factor, "smooth_factor", (torch.bfloat16,), dev)
     _dev(proj_down, "proj_down", (torch.bfloat16,), dev)
-    R = proj_down.shape[1]
+    M, K, R = check_quantize_act_shapes(x, smooth_factor, proj_down)
     qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     ascales = torch.empty((K // 32, mx_scale_rows(M)), dtype=torch.uint8, device=dev)
     lora = torch.empty((M, R), dtype=torch.float32, device=dev)
@@ -282,6 +363,7 @@ def svdq_quantize_weight_mx(w, smooth_factor, hadamard_block=32):
     dev = w.device
     N, K = w.shape
     _dev(smooth_factor, "smooth_factor", (torch.bfloat16,), dev)
+    _shape(smooth_factor, "smooth_factor", (K,))
     qweight = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
     wscales = torch.empty((K // 32, N), dtype=torch.uint8, device=dev)
     st = lib.svdq_quantize_weight_mx(_ptr(w), _ptr(smooth_factor), N, K, int(hadamard_block),
@@ -304,9 +386,10 @@ def svdq_gemm_lowrank_mx(qact, ascales, lora_act, qweight, wscales, proj_up, wcs
     _dev(proj_up, "proj_up", (torch.bfloat16,), dev)
     _dev(wcscales, "wcscales", (torch.bfloat16,), dev)
     _dev(wtscale, "wtscale", (torch.bfloat16,), dev)
-    M, K = qact.shape[0], qact.shape[1] * 2
-    N = qweight.shape[0]
-    R = proj_up.shape[1]
+    if bias is not None:
+        _dev(bias, "bias", (torch.bfloat16,), dev)
+    M, N, K, R = check_gemm_shapes(qact, ascales, lora_act, qweight, wscales, proj_up, wcscales, wtscale, out, bias,
+                                   group=32, scale_rows=mx_scale_rows(qact.shape[0]))
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _dev(y, "y", (torch.bfloat16,), dev)
     if bias is None:
@@ -335,12 +418,15 @@ def svdq_linear_mx(x, layer, hadamard_block=32, workspace=None, out=None):
     _dev(t["wscales"], "wscales", (torch.uint8,), dev)
     for k in ("proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale"):
         _dev(t[k], k, (torch.bfloat16,), dev)
-    N = t["qweight"].shape[0]
-    R = t["proj_up"].shape[1]
+    if layer.get("bias") is not None:
+        _dev(layer["bias"], "bias", (torch.bfloat16,), dev)
+    N, R = check_layer_shapes(M, K, layer, group=32, y=out)
     need = int(lib.svdq_linear_mx_workspace_bytes(M, K, R))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _dev(workspace, "workspace", (torch.uint8,), dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _dev(y, "y", (torch.bfloat16,), dev)
     common = (_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]), _ptr(t["proj_up"]),

@@ -7,11 +7,15 @@ The library lands next to this file, where the binding loads it from.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["csrc/api.cpp", "csrc/quantize.hip", "csrc/gemm.hip", "csrc/gemm_skinny.hip", "csrc/hadamard.hip",
            "csrc/lowrank_split.cpp"]
+# Sources whose kernel choice reads the path-forcing test hooks (see csrc/launch.h).
+HOOKED = ("csrc/gemm.hip", "csrc/gemm_skinny.hip")
+TEST_LIB = "libw4a4_test.so"
 ARCH = os.environ.get("W4A4_ARCH", "gfx950")
 
 
@@ -31,12 +35,7 @@ def flags():
     ]
 
 
-def build(verbose=False, out=None):
-    """Compile every HIP/C++ source into one shared library; returns its path."""
-    out = out or os.path.join(HERE, "libw4a4.so")
-    tmp = out + ".tmp"
-    srcs = [os.path.join(HERE, s) for s in SOURCES]
-    cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,7 +45,39 @@ def build(verbose=False, out=None):
     noise = [ln for ln in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
     if verbose and noise:
         print("\n".join(noise))
-    os.replace(tmp, out)
+
+
+def build(verbose=False, out=None, test_lib=True, jobs=None):
+    """Compile every HIP/C++ source (in parallel, one object each) and link the shared library;
+    returns its path.  With test_lib, also link libw4a4_test.so: the same objects, except the
+    sources with test hooks, which are compiled a second time with W4A4_TEST_HOOKS (tests use it
+    to force kernel variants; nothing else loads it)."""
+    out = out or os.path.join(HERE, "libw4a4.so")
+    objdir = os.path.join(ROOT, "_build", "obj")
+    os.makedirs(objdir, exist_ok=True)
+    base = [f for f in flags() if f != "-shared"]
+    objs, tobjs, cmds = [], [], []
+    for s in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(s) + ".o")
+        objs.append(obj)
+        cmds.append([hipcc()] + base + ["-c", os.path.join(HERE, s), "-o", obj])
+        if test_lib and s in HOOKED:
+            tobj = os.path.join(objdir, os.path.basename(s) + ".hooks.o")
+            tobjs.append(tobj)
+            cmds.append([hipcc()] + base + ["-DW4A4_TEST_HOOKS", "-c", os.path.join(HERE, s), "-o", tobj])
+        else:
+            tobjs.append(obj)
+    # the largest translation units first, so that they do not start last
+    cmds.sort(key=lambda c: -os.path.getsize(c[-3]))
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"]
+    targets = [(out, objs)] + ([(os.path.join(HERE, TEST_LIB), tobjs)] if test_lib else [])
+    for path, ob in targets:
+        tmp = path + ".tmp"
+        _run(link + ob + ["-o", tmp], verbose)
+        os.replace(tmp, path)
     return out
 
 

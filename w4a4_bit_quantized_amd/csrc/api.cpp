@@ -60,6 +60,18 @@ w4a4_status validate_gemm(const void* qact, const void* ascales, const float* lo
 
 }  // namespace
 
+namespace w4a4 {
+
+int quantize_parts(int64_t M, int64_t K) {
+  // Small batches split K across workgroups so that enough CUs stream x; the partial
+  // low-rank sums are added in a fixed order by the consumer.
+  const int64_t n64 = K / 64;
+  if (M > SKINNY_MAX_M || n64 < 16) return 1;
+  return (int)(n64 / 8 < 8 ? n64 / 8 : 8);
+}
+
+}  // namespace w4a4
+
 extern "C" {
 
 const char* w4a4_status_string(int status) {

@@ -35,6 +35,7 @@
 // staged in LDS with coalesced loads.  By default the direct-load kernel is persistent: one
 // workgroup per CU walks its tiles and fetches the next tile's first K-steps during the
 // epilogue (gemm_dma_persist_kernel).
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -1353,33 +1354,39 @@ hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* s
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; concurrent first calls store the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
-// Workgroups of the persistent kernel: as many as run at once (resident workgroups per CU x
-// CUs, a multiple of 8 so that each workgroup's tiles stay on one XCD), at most one per tile;
-// W4A4_GEMM_GRID caps it (tests: several tiles per workgroup at small sizes).  0: not usable.
-template <class KernelFn>
-int persist_grid(KernelFn kernel, int threads, int tiles) {
-  static int per_cu = -1;  // per instantiation; every device here is the same model
+// Workgroups of the persistent kernel with this tile: as many as run at once (resident
+// workgroups per CU x CUs, a multiple of 8 so that each workgroup's tiles stay on one XCD), at
+// most one per tile; the W4A4_GEMM_GRID test hook caps it (several tiles per workgroup at small
+// sizes).  0: not usable.  The occupancy is cached per kernel instantiation and device.
+template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
+int persist_grid(int tiles) {
+  static std::atomic<int> occ[64];  // resident workgroups per CU + 1; 0 = not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int per_cu = occ[dev].load(std::memory_order_relaxed) - 1;
   if (per_cu < 0) {
     int n = 0;
-    per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) == hipSuccess ? n : 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, gemm_dma_persist_kernel<WAVES_M, WAVES_N, FM, FN, LORA>, 64 * WAVES_M * WAVES_N, 0);
+    per_cu = e == hipSuccess ? n : 0;
+    occ[dev].store(per_cu + 1, std::memory_order_relaxed);
   }
-  const int cus = device_cus();
-  int g = per_cu * cus;
+  int g = per_cu * device_cus();
   if (g >= 8) g -= g % 8;
-  if (const char* cap = getenv("W4A4_GEMM_GRID")) {
+  if (const char* cap = test_hook("W4A4_GEMM_GRID")) {
     const int c = atoi(cap);
     if (c > 0 && c < g) g = c;
   }
@@ -1396,14 +1403,15 @@ hipError_t launch_dma(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* 
   dim3 block(T::THREADS);
   if constexpr (!T::ROWWISE) {
     // persistent form: whole 16-byte runs of y rows, |y| addressable by a buffer offset;
-    // W4A4_GEMM_PERSIST=0 keeps one workgroup per tile
-    const char* pe = getenv("W4A4_GEMM_PERSIST");
+    // the W4A4_GEMM_PERSIST=0 test hook keeps one workgroup per tile
+    const char* pe = test_hook("W4A4_GEMM_PERSIST");
     const bool persist = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
                          (int64_t)M * N * 2 <= (int64_t)0x7FFFFFF0 && !(pe && !strcmp(pe, "0"));
     if (persist) {
       auto kern = rb > 0 ? gemm_dma_persist_kernel<WAVES_M, WAVES_N, FM, FN, true>
                          : gemm_dma_persist_kernel<WAVES_M, WAVES_N, FM, FN, false>;
-      const int g = persist_grid(kern, T::THREADS, tiles);
+      const int g = rb > 0 ? persist_grid<WAVES_M, WAVES_N, FM, FN, true>(tiles)
+                           : persist_grid<WAVES_M, WAVES_N, FM, FN, false>(tiles);
       if (g > 0) {
         kern<<<dim3((unsigned)g), block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, y);
         return hipGetLastError();
@@ -1452,7 +1460,7 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
                        const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
                        const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
                        hipStream_t stream) {
-  if (M <= SKINNY_MAX_M && !getenv("W4A4_GEMM_TILE"))
+  if (M <= SKINNY_MAX_M && !test_hook("W4A4_GEMM_TILE"))
     return launch_gemm_skinny(qact, ascales, lora, lora_parts, qweight, wscales, proj_up, wcscales, wtscale, bias, M, N,
                               K, R, y, stream);
   const int rb = (int)((R + 15) / 16);
@@ -1469,12 +1477,12 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R;
   // The three-stage kernel with direct LDS loads needs whole 128-column K-steps and dword-aligned
   // scale quads; W4A4_GEMM_PATH=stage forces the register-staged kernel.
-  const char* path = getenv("W4A4_GEMM_PATH");
+  const char* path = test_hook("W4A4_GEMM_PATH");
   const bool dma = (K % BK) == 0 && (M % 4) == 0 && (N % 4) == 0 &&
                    ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sw)) & 3) == 0 &&
                    !(path && !strcmp(path, "stage"));
   // Pick the best-scoring variant; W4A4_GEMM_TILE (a variant name) forces one.
-  const char* forced = getenv("W4A4_GEMM_TILE");
+  const char* forced = test_hook("W4A4_GEMM_TILE");
   int best = -1;
   double best_score = -1.0;
   for (int i = 0; i < (int)(sizeof(kVariants) / sizeof(kVariants[0])); ++i) {
@@ -1523,7 +1531,7 @@ hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lo
   // 256 tiles by more than the measured per-tile time ratio (2.4: 41 vs 17 us at K = 3072);
   // W4A4_GEMM_TILE=4x4x2x2, 2x4x4x2 (8 waves of 128 x 64), 2x2x4x4 (4 waves of 128 x 128 with
   // register prefetch: half the LDS reads, but measured slower) or 2x2x2x2 forces one
-  const char* forced = getenv("W4A4_GEMM_TILE");
+  const char* forced = test_hook("W4A4_GEMM_TILE");
   const int64_t rounds256 = ((M + 255) / 256 * ((N + 255) / 256) + 255) / 256;
   const int64_t rounds128 = ((M + 127) / 128 * ((N + 127) / 128) + 255) / 256;
   const bool big = forced ? !strcmp(forced, "4x4x2x2") : 2.4 * (double)rounds256 <= (double)rounds128;

@@ -616,9 +616,9 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
   auto yp = static_cast<uint16_t*>(y);
   const bool vec16 = (K % 32) == 0, lo = R > 0;
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R;
-  // W4A4_SKINNY_PATH=wide|stream|regs picks a variant (for tests); by default the wide kernel
+  // the W4A4_SKINNY_PATH=wide|stream|regs test hook picks a variant; by default the wide kernel
   // serves more than 8192 columns, where the 32-row variants would need two workgroups per CU
-  const char* path = getenv("W4A4_SKINNY_PATH");
+  const char* path = test_hook("W4A4_SKINNY_PATH");
   const bool streamed = M <= 16 && (M % 4) == 0 && (K % (2 * SS_CH)) == 0 && K <= 2 * SS_CH * SS_MAXC &&
                         (N % 4) == 0 && ((reinterpret_cast<uintptr_t>(sa) & 3) == 0) &&
                         lora_parts <= SS_MAXPARTS &&

@@ -2,10 +2,20 @@
 // Arguments are already validated by the entry points in api.cpp.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace w4a4 {
+
+// Kernel-path overrides.  Only the test build of the library (compiled with W4A4_TEST_HOOKS)
+// reads them, from the environment, so that tests can force every kernel variant; in the
+// product build every hook is absent and the automatic choice always applies.
+#ifdef W4A4_TEST_HOOKS
+inline const char* test_hook(const char* name) { return getenv(name); }
+#else
+inline const char* test_hook(const char*) { return nullptr; }
+#endif
 
 // Activation (act = true: divide by smooth_factor, low-rank down-projection)
 // or weight (act = false: multiply by smooth_factor) quantizer over `rows` x K.

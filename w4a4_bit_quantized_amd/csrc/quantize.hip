@@ -589,14 +589,6 @@ hipError_t launch_hb(int hb, int rb, dim3 grid, int nunits, int per_part, int ms
 
 }  // namespace
 
-int quantize_parts(int64_t M, int64_t K) {
-  // Small batches split K across workgroups so that enough CUs stream x; the partial
-  // low-rank sums are added in a fixed order by the consumer.
-  const int64_t n64 = K / 64;
-  if (M > SKINNY_MAX_M || n64 < 16) return 1;
-  return (int)(n64 / 8 < 8 ? n64 / 8 : 8);
-}
-
 hipError_t launch_quantize(bool act, const void* x, const void* lam, const void* pd, int64_t M, int64_t K,
                            int64_t R, int hb, int parts, void* q, void* scales, float* lora, hipStream_t stream,
                            bool mx, int64_t scale_stride) {

@@ -45,7 +45,9 @@ typedef enum {
                                or the workspace is too small                      */
   W4A4_ERR_ALIGN = 3,       /* a pointer breaks its required alignment            */
   W4A4_ERR_UNSUPPORTED = 4, /* hadamard_block not in {0,16,32,64,128}, R > 64, or K > W4A4_MAX_K */
-  W4A4_ERR_HIP = 5          /* the HIP runtime reported an error at launch        */
+  W4A4_ERR_HIP = 5,         /* the HIP runtime reported an error at launch        */
+  W4A4_ERR_SCRATCH = 6      /* svdq_linear_noalloc: the sizes need more workspace than its static
+                               device buffer holds (W4A4_NOALLOC_SCRATCH_BYTES)   */
 } w4a4_status;
 
 /* Largest supported correction rank R. */
@@ -218,6 +220,23 @@ w4a4_status svdq_linear_mx_bias(const void* x, const void* qweight, const void* 
                                 const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
                                 int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* ---- The layer without allocation ---------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  svdq_linear_bias (bias may be NULL) with its workspace
+ * in a static device buffer of W4A4_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU
+ * it runs on until the process ends, instead of a caller-provided one.  Same kernels, same
+ * results bit for bit.  Calls whose workspace (svdq_linear_workspace_bytes(M, K, R)) exceeds the
+ * buffer return W4A4_ERR_SCRATCH before any HIP call; other errors as for svdq_linear_bias.  The
+ * call allocates and frees nothing; the buffer's address is looked up once per device (on the
+ * first call with that device current).  Every call on one GPU uses that GPU's one buffer, so
+ * calls that may overlap on a GPU (concurrent streams, host threads) race and must be ordered by
+ * the caller. */
+#define W4A4_NOALLOC_SCRATCH_BYTES (64u << 20)
+w4a4_status svdq_linear_noalloc(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                                const void* proj_up, const void* smooth_factor, const void* wcscales,
+                                const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                                int32_t hadamard_block, void* y, void* stream);
 
 /* ---- Offline low-rank split (host) ----------------------------------------------------------
  * "SVDQuant W4A4" page, "Overview" (four-bit weights and activations plus a small low-rank

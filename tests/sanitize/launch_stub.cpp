@@ -37,4 +37,6 @@ hipError_t launch_hadamard(const void*, int64_t, void*, int64_t, int64_t, int64_
   return hipErrorNoDevice;
 }
 
+void* noalloc_scratch() { return nullptr; }
+
 }  // namespace w4a4

@@ -180,3 +180,26 @@ def test_bias_validation(lib):
     assert lin(P, ws=None) == ERR_NULL
     linm = lambda b: lib.svdq_linear_mx_bias(P, P, P, P, P, P, P, P, b, 16, 64, 256, 32, 32, P, P, 1 << 20, None)
     assert linm(P + 1) == ERR_ALIGN
+
+
+def test_linear_noalloc_validation(lib):
+    """The entry point without allocation: svdq_linear's checks and statuses, then the limit of its
+    static buffer (W4A4_ERR_SCRATCH), all before any HIP call."""
+    f = lib.svdq_linear_noalloc
+
+    def call(x=P, M=16, N=16, K=64, R=8, hb=0, y=P, bias=None):
+        return f(x, P, P, P, P, P, P, P, bias, M, N, K, R, hb, y, None)
+
+    assert call(K=40) == ERR_SHAPE
+    assert call(R=65) == ERR_UNSUPPORTED
+    assert call(hb=8) == ERR_UNSUPPORTED
+    assert call(x=None) == ERR_NULL
+    assert call(y=None) == ERR_NULL
+    assert call(x=P + 8) == ERR_ALIGN
+    assert call(bias=P + 1) == ERR_ALIGN
+    assert call(M=0) == OK and call(N=0) == OK
+    # 64 MiB holds M * K / 2 + M * K / 16 + 4 M R bytes (each part 256-byte aligned)
+    assert call(M=4096, K=12288, R=32) != 6          # 28.9 MB: fits
+    assert call(M=8192, K=16384, R=32) == 6          # 77 MB: refused
+    assert call(M=8192, K=16384, R=32, x=None) == ERR_NULL  # other errors are reported first
+    assert lib.w4a4_status_string(6)

@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 STATUS_NAMES = {0: "W4A4_OK", 1: "W4A4_ERR_NULL", 2: "W4A4_ERR_SHAPE", 3: "W4A4_ERR_ALIGN",
-                4: "W4A4_ERR_UNSUPPORTED", 5: "W4A4_ERR_HIP"}
+                4: "W4A4_ERR_UNSUPPORTED", 5: "W4A4_ERR_HIP", 6: "W4A4_ERR_SCRATCH"}
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -47,6 +47,8 @@ SIGNATURES = {
                                                  _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "svdq_lowrank_split": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, ctypes.c_uint64,
                                           _c_i32, _c_p, _c_p, _c_p, _c_p]),
+    "svdq_linear_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                           _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p]),
     "svdq_linear_mx_bias": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                            _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_p, _c_p, ctypes.c_size_t,
                                            _c_p]),
@@ -322,6 +324,37 @@ def svdq_linear(x, layer, hadamard_block=0, workspace=None, out=None):
         _dev(bias, "bias", (torch.bfloat16,), dev)
         st = lib.svdq_linear_bias(*common, _ptr(bias), *tail)
     _check(st, "svdq_linear")
+    return y.reshape(*lead, N)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # W4A4_NOALLOC_SCRATCH_BYTES
+
+
+def svdq_linear_noalloc(x, layer, hadamard_block=0, out=None):
+    """``svdq_linear`` through the entry point without allocation: the library's static device
+    workspace instead of a caller-provided one (the binding still allocates ``out`` unless given)."""
+    torch = _torch()
+    lib = load_library()
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    _dev(x2, "x", (torch.bfloat16,))
+    dev = x2.device
+    M, K = x2.shape
+    t = {k: layer[k] for k in LAYER_KEYS}
+    _dev(t["qweight"], "qweight", _bytes_dtypes(), dev)
+    _dev(t["wscales"], "wscales", _scale_dtypes(), dev)
+    for k in ("proj_down", "proj_up", "smooth_factor", "wcscales", "wtscale"):
+        _dev(t[k], k, (torch.bfloat16,), dev)
+    bias = layer.get("bias")
+    if bias is not None:
+        _dev(bias, "bias", (torch.bfloat16,), dev)
+    N, R = check_layer_shapes(M, K, layer, group=16, y=out)
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _dev(y, "y", (torch.bfloat16,), dev)
+    st = lib.svdq_linear_noalloc(_ptr(x2), _ptr(t["qweight"]), _ptr(t["wscales"]), _ptr(t["proj_down"]),
+                                 _ptr(t["proj_up"]), _ptr(t["smooth_factor"]), _ptr(t["wcscales"]), _ptr(t["wtscale"]),
+                                 _ptr(bias), M, N, K, R, int(hadamard_block), _ptr(y), _stream(dev))
+    _check(st, "svdq_linear_noalloc")
     return y.reshape(*lead, N)
 
 

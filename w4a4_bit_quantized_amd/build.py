@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["csrc/api.cpp", "csrc/quantize.hip", "csrc/gemm.hip", "csrc/gemm_skinny.hip", "csrc/hadamard.hip",
-           "csrc/lowrank_split.cpp"]
+           "csrc/lowrank_split.cpp", "csrc/noalloc.hip"]
 # Sources whose kernel choice reads the path-forcing test hooks (see csrc/launch.h).
 HOOKED = ("csrc/gemm.hip", "csrc/gemm_skinny.hip")
 TEST_LIB = "libw4a4_test.so"

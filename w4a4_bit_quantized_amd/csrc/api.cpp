@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
+#include <cstdint>
 
 #include "launch.h"
 
@@ -82,6 +83,7 @@ const char* w4a4_status_string(int status) {
     case W4A4_ERR_ALIGN: return "a pointer breaks its required alignment";
     case W4A4_ERR_UNSUPPORTED: return "unsupported hadamard_block, or rank or K above the compiled maximum";
     case W4A4_ERR_HIP: return "HIP runtime error at launch";
+    case W4A4_ERR_SCRATCH: return "the sizes need more workspace than the static buffer of svdq_linear_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -137,10 +139,16 @@ size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int64_t R) {
   return align256(m * k / 2) + align256(k / 16 * m) + align256(parts * m * r * sizeof(float));
 }
 
-w4a4_status svdq_linear_bias(const void* x, const void* qweight, const void* wscales, const void* proj_down,
-                             const void* proj_up, const void* smooth_factor, const void* wcscales,
-                             const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
-                             int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// svdq_linear's validation and, when `launch`, its two launches.  With launch == false nothing
+// touches HIP and the workspace pointer is only checked (never dereferenced).
+w4a4_status linear_impl(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                        const void* proj_up, const void* smooth_factor, const void* wcscales, const void* wtscale,
+                        const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, int32_t hadamard_block, void* y,
+                        void* workspace, size_t workspace_bytes, void* stream, bool launch) {
   w4a4_status st = check_k_rank_block(K, R, hadamard_block);
   if (st != W4A4_OK) return st;
   if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return W4A4_ERR_SHAPE;
@@ -159,7 +167,7 @@ w4a4_status svdq_linear_bias(const void* x, const void* qweight, const void* wsc
   st = validate_quantize_act(x, smooth_factor, proj_down, M, K, R, hadamard_block, qact, ascales, lora);
   if (st != W4A4_OK) return st;
   st = validate_gemm(qact, ascales, lora, qweight, wscales, proj_up, wcscales, wtscale, M, N, K, R, y);
-  if (st != W4A4_OK) return st;
+  if (st != W4A4_OK || !launch) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const int parts = w4a4::quantize_parts(M, K);
@@ -170,12 +178,43 @@ w4a4_status svdq_linear_bias(const void* x, const void* qweight, const void* wsc
                                     N, K, R, y, s));
 }
 
+}  // namespace
+
+extern "C" {
+
+w4a4_status svdq_linear_bias(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                             const void* proj_up, const void* smooth_factor, const void* wcscales,
+                             const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                             int32_t hadamard_block, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_impl(x, qweight, wscales, proj_down, proj_up, smooth_factor, wcscales, wtscale, bias, M, N, K, R,
+                     hadamard_block, y, workspace, workspace_bytes, stream, true);
+}
+
 w4a4_status svdq_linear(const void* x, const void* qweight, const void* wscales, const void* proj_down,
                         const void* proj_up, const void* smooth_factor, const void* wcscales, const void* wtscale,
                         int64_t M, int64_t N, int64_t K, int64_t R, int32_t hadamard_block, void* y, void* workspace,
                         size_t workspace_bytes, void* stream) {
   return svdq_linear_bias(x, qweight, wscales, proj_down, proj_up, smooth_factor, wcscales, wtscale, nullptr, M, N, K,
                           R, hadamard_block, y, workspace, workspace_bytes, stream);
+}
+
+w4a4_status svdq_linear_noalloc(const void* x, const void* qweight, const void* wscales, const void* proj_down,
+                                const void* proj_up, const void* smooth_factor, const void* wcscales,
+                                const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                                int32_t hadamard_block, void* y, void* stream) {
+  // Every check of svdq_linear_bias first, with a stand-in address for the static buffer (it is
+  // not dereferenced), so that invalid calls get the same status and touch no HIP state; then the
+  // buffer's limit; then its address on the current device, and the same launches.
+  const size_t cap = (size_t)W4A4_NOALLOC_SCRATCH_BYTES;
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t{256});
+  w4a4_status st = linear_impl(x, qweight, wscales, proj_down, proj_up, smooth_factor, wcscales, wtscale, bias, M, N,
+                               K, R, hadamard_block, y, stand_in, SIZE_MAX, stream, false);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if (svdq_linear_workspace_bytes(M, K, R) > cap) return W4A4_ERR_SCRATCH;
+  void* ws = w4a4::noalloc_scratch();
+  if (ws == nullptr) return W4A4_ERR_HIP;
+  return linear_impl(x, qweight, wscales, proj_down, proj_up, smooth_factor, wcscales, wtscale, bias, M, N, K, R,
+                     hadamard_block, y, ws, cap, stream, true);
 }
 
 }  // extern "C"

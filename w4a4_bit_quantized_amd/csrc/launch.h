@@ -60,4 +60,8 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
 hipError_t launch_hadamard(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols, int block,
                            int dtype, float norm, hipStream_t stream);
 
+// Device address of the static workspace of svdq_linear_noalloc on the current device (looked up
+// once per device), or NULL when the lookup fails.
+void* noalloc_scratch();
+
 }  // namespace w4a4

@@ -56,9 +56,11 @@ def sha_of(paths):
 
 
 KERNEL_SOURCES = {
-    "gemm": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
+    "gemm": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/gemm_common.h",
+             "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "gemm_skinny": ["w4a4_bit_quantized_amd/csrc/gemm_skinny.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
-    "gemm_mx": ["w4a4_bit_quantized_amd/csrc/gemm.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
+    "gemm_mx": ["w4a4_bit_quantized_amd/csrc/gemm_mx.hip", "w4a4_bit_quantized_amd/csrc/gemm_common.h",
+                "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "hadamard": ["w4a4_bit_quantized_amd/csrc/hadamard.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "quantize": ["w4a4_bit_quantized_amd/csrc/quantize.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
 }

@@ -12,9 +12,9 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["csrc/api.cpp", "csrc/quantize.hip", "csrc/gemm.hip", "csrc/gemm_skinny.hip", "csrc/hadamard.hip",
-           "csrc/lowrank_split.cpp", "csrc/noalloc.hip"]
+           "csrc/lowrank_split.cpp", "csrc/noalloc.hip", "csrc/gemm_mx.hip"]
 # Sources whose kernel choice reads the path-forcing test hooks (see csrc/launch.h).
-HOOKED = ("csrc/gemm.hip", "csrc/gemm_skinny.hip")
+HOOKED = ("csrc/gemm.hip", "csrc/gemm_skinny.hip", "csrc/gemm_mx.hip")
 TEST_LIB = "libw4a4_test.so"
 ARCH = os.environ.get("W4A4_ARCH", "gfx950")
 

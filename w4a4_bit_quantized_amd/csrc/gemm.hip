@@ -40,122 +40,25 @@
 #include <cstring>
 
 #include "device_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace w4a4 {
 
+// Compute units of the current device (cached per device; concurrent first calls store the same value).
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 namespace {
-
-constexpr int BK = 128;            // K columns per stage (8 groups of 16)
-constexpr int CODE_STRIDE = 80;    // LDS bytes per code row: 64 data + 16 pad (conflict-free b128 reads)
-
-// Output tile (tm, tn) of workgroup b among G tiles of a tiles_m x tiles_n grid.  Workgroups are
-// dispatched to the 8 XCDs in turn; each XCD takes a contiguous range of a grouped order that
-// walks GROUP_M tile rows column by column, so the tiles one XCD runs at a time share a few
-// activation and weight panels in its L2.
-constexpr int GROUP_M = 8;
-
-__device__ __forceinline__ void tile_of(int b, int G, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int q = G / 8, r = G % 8, x = b % 8, l = b / 8;
-  const int p = x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;  // position in the grouped order
-  const int group = p / (GROUP_M * tiles_n);
-  const int first_m = group * GROUP_M;
-  const int rows = min(GROUP_M, tiles_m - first_m);
-  const int in = p - group * GROUP_M * tiles_n;
-  tm = first_m + in % rows;
-  tn = in / rows;
-}
-
-template <int WAVES_M, int WAVES_N, int FM, int FN>
-struct Tile {
-  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
-  static constexpr int WM = WAVES_M, WN = WAVES_N, FRAG_M = FM, FRAG_N = FN;
-  static constexpr int BM = WAVES_M * FM * 32;
-  static constexpr int BN = WAVES_N * FN * 32;
-  static constexpr int ROWS = BM + BN;  // activation rows, then weight rows, in LDS
-  static constexpr int A_CPT = (BM * 4 + THREADS - 1) / THREADS;  // 16-byte code chunks per thread
-  static constexpr int B_CPT = (BN * 4 + THREADS - 1) / THREADS;
-  static constexpr int SA_PT = (2 * BM + THREADS - 1) / THREADS;  // (group, 4-row quad) scale words per thread
-  static constexpr int SB_PT = (2 * BN + THREADS - 1) / THREADS;
-  static constexpr int SCALE_BYTES = 8 * ROWS * 2;  // f16 scales laid out [group][row]
-  static constexpr int STAGE_BYTES = ROWS * CODE_STRIDE + SCALE_BYTES;
-  // Epilogue operands, staged in the stage buffers after the K loop: L hi and lo parts
-  // [BM][EPI_RS] bf16, proj_up [BN][EPI_RS] bf16, the column scale [BN] f32 and the bias [BN] f32.
-  // The rank stride holds the compiled maximum rank plus 8: 144-byte rows put the 16-byte reads
-  // of 16 consecutive rows on distinct banks.
-  static constexpr int EPI_RS = 64 + 8;
-  static constexpr int EPI_BYTES = BM * EPI_RS * 2 * 2 + BN * EPI_RS * 2 + BN * 8;
-  // Waves with 16 or more accumulator fragments (which fill the accumulation registers) finish
-  // one fragment row at a time, each wave through a 32-row store region of its own placed after
-  // the epilogue operands.
-  static constexpr bool ROWWISE = FM * FN >= 16;
-  static constexpr int EPI_LDS = EPI_BYTES + (ROWWISE ? WAVES_M * WAVES_N * 32 * FN * 64 : 0);
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_LDS ? 2 * STAGE_BYTES : EPI_LDS;
-};
-
-// Stage a tile's epilogue operands in LDS: the column scales wcscales * wtscale and the bias
-// (zero without one) when r_lo == 0, and for the ranks [r_lo, r_hi) (columns r - r_lo of the
-// rank-strided arrays) the low-rank activations summed over their `parts` partial sums (in
-// order) and split into bf16 hi + lo parts, and proj_up.  Padded ranks and rows past M or N are
-// zero or clamped.  Each thread issues all its loads of a 16-rank block before storing any of
-// them.
-template <class T, bool LORA>
-__device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int r_lo, int r_hi, int t, int m0, int n0,
-                                               int M, int N, int R, int parts, const float* __restrict__ lora,
-                                               const uint16_t* __restrict__ pu, const uint16_t* __restrict__ wcs,
-                                               const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias) {
-  uint16_t* l_hi = reinterpret_cast<uint16_t*>(base);
-  uint16_t* l_lo = l_hi + T::BM * rs;
-  uint16_t* p_lds = l_lo + T::BM * rs;
-  float* c_lds = reinterpret_cast<float*>(p_lds + T::BN * rs);
-  float* b_lds = c_lds + T::BN;
-  if (r_lo == 0) {
-    const float ts = bf16_bits_to_f32(wts[0]);
-    for (int c = t; c < T::BN; c += T::THREADS) {
-      const int n = n0 + c;
-      c_lds[c] = n < N ? bf16_bits_to_f32(wcs[n]) * ts : 0.0f;
-      b_lds[c] = (bias != nullptr && n < N) ? bf16_bits_to_f32(bias[n]) : 0.0f;
-    }
-  }
-  if (!LORA) return;
-  constexpr int LI = (T::BM * 16 + T::THREADS - 1) / T::THREADS;
-  constexpr int PI = (T::BN * 16 + T::THREADS - 1) / T::THREADS;
-  for (int r0 = r_lo; r0 < r_hi; r0 += 16) {
-    float f[LI];
-    uint32_t pw[PI];
-#pragma unroll
-    for (int u = 0; u < LI; ++u) {
-      const int idx = t + u * T::THREADS;
-      const int rr = min(idx >> 4, T::BM - 1), r = r0 + (idx & 15);
-      const size_t at = (size_t)min(m0 + rr, M - 1) * R + (r < R ? r : 0);
-      float acc_l = 0.0f;
-      for (int p = 0; p < parts; ++p) acc_l += lora[(size_t)p * M * R + at];
-      f[u] = r < R ? acc_l : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < PI; ++u) {
-      const int idx = t + u * T::THREADS;
-      const int rr = min(idx >> 4, T::BN - 1), r = r0 + (idx & 15);
-      const uint32_t v = pu[(size_t)min(n0 + rr, N - 1) * R + (r < R ? r : 0)];
-      pw[u] = r < R ? v : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < LI; ++u) {
-      const int idx = t + u * T::THREADS;
-      if ((T::BM * 16) % T::THREADS == 0 || idx < T::BM * 16) {
-        const int rr = idx >> 4, r = r0 - r_lo + (idx & 15);
-        const uint32_t hb = f32_to_bf16_bits(f[u]);
-        l_hi[rr * rs + r] = (uint16_t)hb;
-        l_lo[rr * rs + r] = (uint16_t)f32_to_bf16_bits(f[u] - bf16_bits_to_f32(hb));  // exact remainder
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PI; ++u) {
-      const int idx = t + u * T::THREADS;
-      if ((T::BN * 16) % T::THREADS == 0 || idx < T::BN * 16) p_lds[(idx >> 4) * rs + r0 - r_lo + (idx & 15)] = (uint16_t)pw[u];
-    }
-  }
-}
 
 // Global -> register -> LDS staging of one K-step.  Per-thread offsets are loop invariant;
 // each K-step only moves the uniform base pointers.  Rows past M (or N) read a clamped valid
@@ -304,13 +207,6 @@ struct Stager {
   }
 };
 
-// Two float32 -> packed bf16 pair, round to nearest even (hardware convert).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t v = __builtin_convertvector(float2_t{a, b}, bf16x2_t);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 // One K-step of a wave from its operands already in registers: 8 sub-steps, each one
 // v_mfma_f32_32x32x16_f16 per (i, j) fragment pair; sub-step kk + 1 is decoded while the MFMAs
 // of sub-step kk run.  Sub-step kk covers K-columns 64h + 8kk .. +8 of the stage (lane half h),
@@ -344,208 +240,6 @@ __device__ __forceinline__ void mma_stage(float16_t (&acc)[FM][FN], const uint32
 #pragma unroll
       for (int j = 0; j < FN; ++j) bv[j] = bn[j];
     }
-  }
-}
-
-// Epilogue of a tile: stage the operands in LDS (`lds` must be free; it is left in use), then
-// acc *= wcscales[n] * wtscale, add L @ proj_up^T on the matrix cores, round to bf16 and store.
-// acc[i][j][4q + e] is y[m, n] with m = mb + i*32 + l32, n = nb + j*32 + 8q + 4h + e.
-template <class T, bool LORA>
-__device__ __forceinline__ void epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N], uint8_t* lds, int t, int m0,
-                                         int n0, int M, int N, int R, int parts, const float* __restrict__ lora,
-                                         const uint16_t* __restrict__ pu, const uint16_t* __restrict__ wcs,
-                                         const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias,
-                                         uint16_t* __restrict__ y) {
-  constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
-  constexpr int rs = T::EPI_RS;  // rank stride of the staged operands
-  const int lane = t & 63, wave = t >> 6;
-  const int wm = wave / T::WN, wn = wave % T::WN;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank
-  stage_epilogue<T, LORA>(lds, rs, 0, rp, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
-  __syncthreads();
-  const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
-  const uint16_t* l_hi = reinterpret_cast<const uint16_t*>(lds);
-  const uint16_t* l_lo = l_hi + T::BM * rs;
-  const uint16_t* p_lds = l_lo + T::BM * rs;
-  const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
-  const float* b_lds = c_lds + T::BN;
-  const bool has_bias = bias != nullptr;
-  if constexpr (T::ROWWISE) {
-    // Same arithmetic, in the same order per element, one fragment at a time; each fragment
-    // row then leaves through the wave's store region (16-byte stores) or, when y rows are not
-    // whole 16-byte runs, directly.
-    constexpr int RSB = FN * 64, CPR = FN * 4;
-    uint8_t* reg = lds + T::EPI_BYTES + wave * 32 * RSB;
-    const bool coalesce = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
-    const bool n4 = (N & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = wm * FM * 32 + i * 32 + l32;
-      const int m = mb + i * 32 + l32;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        float16_t a = acc[i][j];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[4 * q + e] *= c[e];
-        }
-        if (LORA) {
-          for (int r0 = 0; r0 < rp; r0 += 16) {
-            const bf16x8_t pv =
-                *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * rs + r0 + 8 * h);
-            const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * rs + r0 + 8 * h);
-            const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
-            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv, lhi, a, 0, 0, 0);
-            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv, llo, a, 0, 0, 0);
-          }
-        }
-        if (has_bias) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4_t b = *reinterpret_cast<const float4_t*>(b_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[4 * q + e] += b[e];
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t p0 = pack_bf16x2(a[4 * q], a[4 * q + 1]);
-          const uint32_t p1 = pack_bf16x2(a[4 * q + 2], a[4 * q + 3]);
-          const int n = nb + j * 32 + 8 * q + 4 * h;
-          if (coalesce) {
-            const int ch = 4 * j + q;
-            *reinterpret_cast<u32x2_t*>(reg + l32 * RSB + 16 * ((ch + (l32 >> 1)) % CPR) + 8 * h) = u32x2_t{p0, p1};
-          } else if (m < M) {
-            uint16_t* yrow = y + (size_t)m * N;
-            if (n4) {
-              if (n < N) *reinterpret_cast<u32x2_t*>(yrow + n) = u32x2_t{p0, p1};
-            } else {
-              const uint16_t v[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (n + e < N) yrow[n + e] = v[e];
-            }
-          }
-        }
-      }
-      if (coalesce) {
-        wave_lds_sync();
-#pragma unroll
-        for (int it = 0; it < CPR / 2; ++it) {
-          const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR));
-          const int mr = mb + i * 32 + r, n = nb + 8 * ch;
-          if (mr < M && n < N) *reinterpret_cast<u32x4_t*>(y + (size_t)mr * N + n) = v;
-        }
-        wave_lds_sync();  // the region is rewritten by the next fragment row
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
-    }
-  if (LORA) {
-    for (int r0 = 0; r0 < rp; r0 += 16) {
-      bf16x8_t pv[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        pv[j] = *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * rs + r0 + 8 * h);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * FM * 32 + i * 32 + l32;
-        const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * rs + r0 + 8 * h);
-        const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], llo, acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-  }
-  if (has_bias) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4_t b = *reinterpret_cast<const float4_t*>(b_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] += b[e];
-      }
-  }
-  if ((N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
-    // Coalesced stores: each wave passes its rounded tile through a private LDS region (IC fragment
-    // rows at a time) and writes whole 16-byte runs of y rows (a wave instruction covers
-    // 64 / CPR rows x 64 FN contiguous bytes).  Chunk ch of region row r sits at position
-    // (ch + r / 2) % CPR, which keeps both the 8-byte writes and the 16-byte reads on distinct banks.
-    constexpr int WAVES = T::WM * T::WN;
-    constexpr int RSB = FN * 64;  // bytes per region row
-    constexpr int CPR = FN * 4;   // 16-byte chunks per region row
-    constexpr int IC = WAVES * FM * 32 * RSB <= T::EPI_BYTES ? FM
-                       : ((FM % 2) == 0 && WAVES * (FM / 2) * 32 * RSB <= T::EPI_BYTES) ? FM / 2 : 1;
-    static_assert(WAVES * IC * 32 * RSB <= T::EPI_BYTES, "store regions fit the epilogue's LDS");
-    __syncthreads();  // every wave is done with the staged operands
-    uint8_t* reg = lds + wave * IC * 32 * RSB;
-#pragma unroll
-    for (int i0 = 0; i0 < FM; i0 += IC) {
-#pragma unroll
-      for (int i = i0; i < i0 + IC; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = (i - i0) * 32 + l32, ch = 4 * j + q;
-            const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-            const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            *reinterpret_cast<u32x2_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR) + 8 * h) = u32x2_t{p0, p1};
-          }
-      wave_lds_sync();
-#pragma unroll
-      for (int it = 0; it < IC * CPR / 2; ++it) {
-        const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR));
-        const int m = mb + i0 * 32 + r, n = nb + 8 * ch;
-        if (m < M && n < N) *reinterpret_cast<u32x4_t*>(y + (size_t)m * N + n) = v;
-      }
-      wave_lds_sync();  // the region is rewritten by the next fragment rows
-    }
-    return;
-  }
-  const bool n4 = (N & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = mb + i * 32 + l32;
-    if (m >= M) continue;
-    uint16_t* yrow = y + (size_t)m * N;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nb + j * 32 + 8 * q + 4 * h;
-        const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-        const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        if (n4) {
-          if (n < N) *reinterpret_cast<u32x2_t*>(yrow + n) = u32x2_t{p0, p1};
-        } else {
-          const uint16_t v[4] = {(uint16_t)p0, (uint16_t)(p0 >> 16), (uint16_t)p1, (uint16_t)(p1 >> 16)};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) yrow[n + e] = v[e];
-        }
-      }
   }
 }
 
@@ -649,11 +343,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 //    its half with one 16-byte read and picks its row's byte out of each dword.
 // Rows past the tile's valid ones (and the padding up to whole instructions) read clamped
 // valid rows and are never stored.
-// 16-byte chunk position of a code row's chunk 0 in LDS (chunk c goes to c ^ code_swizzle(r)):
-// rows r and r + 4 share banks (64-byte rows, 256 bytes of banks), so the four rows of a bank
-// line take distinct positions.
-__device__ __forceinline__ int code_swizzle(int row) { return (row >> 2) & 3; }
-
 template <class T>
 struct DmaTile {
   static constexpr int WAVES = T::WM * T::WN;
@@ -667,34 +356,6 @@ struct DmaTile {
   static constexpr int LDS_BYTES = 3 * STAGE > T::EPI_LDS ? 3 * STAGE : T::EPI_LDS;
   static_assert(T::BM % 16 == 0 && T::ROWS % 16 == 0, "whole 16-row blocks");
 };
-
-// Wait until at most N vector-memory operations of this wave are outstanding and all its LDS
-// operations are done, then join the workgroup barrier.  The compiler may not move memory
-// operations across it.
-template <int N>
-__device__ __forceinline__ void vm_wait_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Issue one K-step's direct loads of a wave: ROUNDS code instructions (16 bytes per lane) and
-// SROUNDS scale instructions (4 bytes per lane) into the stage at `stage`.
-template <class D>
-__device__ __forceinline__ void dma_issue(uint8_t* stage, int wave, uint32_t kb0, size_t g0,
-                                          const uint8_t* const* c_base, const uint32_t* c_off,
-                                          const uint8_t* const* s_base, const uint32_t* s_off,
-                                          const uint32_t* s_stride) {
-#pragma unroll
-  for (int r = 0; r < D::ROUNDS; ++r)
-    __builtin_amdgcn_global_load_lds(c_base[r] + kb0 + c_off[r],
-                                     (lds_void*)(stage + (r * D::ROUND_ROWS + wave * 16) * 64), 16, 0, 0);
-#pragma unroll
-  for (int r = 0; r < D::SROUNDS; ++r)
-    __builtin_amdgcn_global_load_lds(s_base[r] + g0 * s_stride[r] + s_off[r],
-                                     (lds_void*)(stage + D::SCALE_OFF + (r * D::WAVES + wave) * 256), 4, 0, 0);
-}
 
 // Per-tile addresses of a wave's direct loads: the code chunk of each round (tile row clamped to
 // a valid row, swizzled 16-byte chunk) and the scale dword of each round (LDS dword index d ->
@@ -847,143 +508,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 // them in: the stores drain while K-steps 0 and 1 run on the matrix cores.  Loads and stores
 // of a wave complete in issue order on this target (the compiler's own waits assume the same).
 // Needs whole 16-byte runs of y rows (N % 8 == 0, y 16-byte aligned) and |y| below 2^31 bytes.
-template <class T, class D = DmaTile<T>>
-struct PersistTile {
-  static constexpr int RW = 32;      // ranks staged per pass
-  static constexpr int RS = RW + 8;  // rank stride of the staged operands: 80-byte rows put the 16-byte
-                                     // reads of 16 consecutive rows on distinct banks
-  static constexpr int WAVES = T::WM * T::WN;
-  static constexpr int RSB = T::FRAG_N * 64, CPR = T::FRAG_N * 4;  // store region row: bytes, 16-byte chunks
-  static constexpr int OPS = T::BM * RS * 4 + T::BN * RS * 2 + T::BN * 8;  // L hi + lo, proj_up, scale, bias
-  static constexpr int REGIONS = WAVES * 32 * RSB;  // one 32-row fragment row per wave
-  static constexpr int E_OFF = 2 * D::STAGE;
-  static constexpr int E_BYTES = OPS > REGIONS ? OPS : REGIONS;
-  static constexpr int LDS_BYTES = 3 * D::STAGE > E_OFF + E_BYTES ? 3 * D::STAGE : E_OFF + E_BYTES;
-  static constexpr int ST = T::FRAG_M * CPR / 2;  // y stores of a wave per tile
-  static_assert(!T::ROWWISE, "whole-tile epilogue");
-  static_assert(D::LOADS + ST < 64, "vmcnt range");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
-};
-
-// N buffer stores that the hardware drops (offsets from 2^31 up, past any y the persistent kernels
-// accept), each to its own offset so that none is merged with another.
-template <int N>
-__device__ __forceinline__ void drop_stores(__amdgpu_buffer_rsrc_t yr) {
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, yr, (int)(0x80000000u + 16u * (uint32_t)i), 0, 0);
-}
-
-// LDS-only barrier: waits for this wave's LDS operations, not for its loads or stores in flight.
-__device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Epilogue of one tile in the persistent kernels (as `epilogue`, whole-tile form): the operands are
-// staged in a region E after stage slots 0 and 1, 32 ranks per pass; `prefetch` runs once the first
-// pass is staged (it issues the next tile's first K-steps into slots 0 and 1); y leaves through
-// exactly P::ST buffer stores per wave, chunks outside y at an offset the hardware drops.
-template <class T, class P, bool LORA, class Prefetch>
-__device__ __forceinline__ void persist_epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N], uint8_t* lds, int wave, int lane,
-                                                 int m0, int n0, int M, int N, int R, int parts,
-                                                 const float* __restrict__ lora, const uint16_t* __restrict__ pu,
-                                                 const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts,
-                                                 const uint16_t* __restrict__ bias, __amdgpu_buffer_rsrc_t yr,
-                                                 Prefetch&& prefetch) {
-  constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
-  constexpr int rw = P::RW, rs = P::RS, RSB = P::RSB, CPR = P::CPR;
-  const int wm = wave / T::WN, wn = wave % T::WN;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int t = wave * 64 + lane;
-  const int rp = LORA ? 16 * ((R + 15) / 16) : 0;  // padded rank
-  uint8_t* const E = lds + P::E_OFF;
-  const uint16_t* l_hi = reinterpret_cast<const uint16_t*>(E);
-  const uint16_t* l_lo = l_hi + T::BM * rs;
-  const uint16_t* p_lds = l_lo + T::BM * rs;
-  const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
-  const float* b_lds = c_lds + T::BN;
-  // epilogue operands, first pass; then the caller's prefetch of the next tile
-  stage_epilogue<T, LORA>(E, rs, 0, min(rp, rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
-  prefetch();
-  lds_only_barrier();
-
-  // acc *= wcscales * wtscale; + L @ proj_up^T (passes of 32 ranks); + bias (as in `epilogue`)
-  const int mb = m0 + wm * FM * 32, nb = n0 + wn * FN * 32;
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4_t c = *reinterpret_cast<const float4_t*>(c_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] *= c[e];
-    }
-  if (LORA) {
-    for (int lo = 0; lo < rp; lo += rw) {
-      if (lo > 0) {
-        lds_only_barrier();  // every wave is done with the previous pass
-        stage_epilogue<T, LORA>(E, rs, lo, min(rp, lo + rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
-        lds_only_barrier();
-      }
-      for (int r0 = 0; r0 < min(rp - lo, rw); r0 += 16) {
-        bf16x8_t pv[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          pv[j] = *reinterpret_cast<const bf16x8_t*>(p_lds + (wn * FN * 32 + j * 32 + l32) * rs + r0 + 8 * h);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int row = wm * FM * 32 + i * 32 + l32;
-          const bf16x8_t lhi = *reinterpret_cast<const bf16x8_t*>(l_hi + row * rs + r0 + 8 * h);
-          const bf16x8_t llo = *reinterpret_cast<const bf16x8_t*>(l_lo + row * rs + r0 + 8 * h);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], lhi, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv[j], llo, acc[i][j], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
-  if (bias != nullptr) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4_t b = *reinterpret_cast<const float4_t*>(b_lds + wn * FN * 32 + j * 32 + 8 * q + 4 * h);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][j][4 * q + e] += b[e];
-      }
-  }
-  lds_only_barrier();  // every wave is done with the staged operands: E becomes store regions
-
-  // one fragment row at a time through the wave's region (chunk ch of region row r at
-  // (ch + r / 2) % CPR), then whole 16-byte runs of y rows
-  uint8_t* reg = E + wave * 32 * RSB;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int ch = 4 * j + q;
-        const uint32_t p0 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-        const uint32_t p1 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        *reinterpret_cast<u32x2_t*>(reg + l32 * RSB + 16 * ((ch + (l32 >> 1)) % CPR) + 8 * h) = u32x2_t{p0, p1};
-      }
-    wave_lds_sync();
-#pragma unroll
-    for (int it = 0; it < CPR / 2; ++it) {
-      const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
-      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(reg + r * RSB + 16 * ((ch + (r >> 1)) % CPR));
-      const int m = mb + i * 32 + r, n = nb + 8 * ch;
-      const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u;
-      __builtin_amdgcn_raw_buffer_store_b128(val, yr, (int)off, 0, 0);
-    }
-    wave_lds_sync();  // the region is rewritten by the next fragment row
-  }
-}
-
 template <int WAVES_M, int WAVES_N, int FM, int FN, bool LORA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kernel(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
@@ -992,7 +516,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
     uint16_t* __restrict__ y) {
   using T = Tile<WAVES_M, WAVES_N, FM, FN>;
   using D = DmaTile<T>;
-  using P = PersistTile<T>;
+  using P = PersistTile<T, D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[P::LDS_BYTES];
 
   const int lane0 = (int)threadIdx.x & 63;
@@ -1055,285 +579,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
   }
 }
 
-// ---- MXFP4 variant (rotate notes, section 3.3: FP-Quant mxfp4, matmul_mxf4_bf16) ----------
-// Codes as above; one E8M0 scale per 32 K-columns, (K/32, rows) tensors whose dwords are 4
-// consecutive rows of one block.  The product runs on the scaled FP4 matrix instruction
-// v_mfma_scale_f32_32x32x64_f8f6f4, which takes the packed E2M1 codes directly and applies a
-// power-of-two scale per row and 32-column block: no decode.  Lane l of an operand supplies row
-// l % 32, K-columns 32 (l / 32) .. +32 of the instruction's 64 (16 bytes in the first four
-// registers) and, in byte `opsel` of its scale register, the E8M0 byte of that row and block.
-// A K-step of 128 columns is two instructions; lane half h reads code chunks h and 2 + h of
-// its row and the scales of blocks h and 2 + h.  The accumulator layout equals the f16
-// kernel's, so the epilogue is shared.
-template <class T, int S>
-struct DmaTileMx {
-  static constexpr int STAGES = S;                // K-steps resident in LDS; S - 1 of them in flight
-  static constexpr int WAVES = T::WM * T::WN;
-  static constexpr int ROUND_ROWS = 16 * WAVES;
-  static constexpr int ROUNDS = (T::ROWS + ROUND_ROWS - 1) / ROUND_ROWS;
-  static constexpr int SDW = T::ROWS;             // scale dwords per K-step: ROWS/4 quads x 4 blocks
-  static constexpr int SROUNDS = (SDW + 64 * WAVES - 1) / (64 * WAVES);
-  static constexpr int SCALE_OFF = ROUNDS * ROUND_ROWS * 64;
-  static constexpr int STAGE = SCALE_OFF + SROUNDS * WAVES * 256;
-  static constexpr int LOADS = ROUNDS + SROUNDS;
-  static constexpr int LDS_BYTES = S * STAGE > T::EPI_LDS ? S * STAGE : T::EPI_LDS;
-  static_assert(T::BM % 16 == 0 && T::ROWS % 16 == 0, "whole 16-row blocks");
-  static_assert(S >= 3 && (S - 2) * LOADS < 64, "vmcnt range");
-};
-
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Read a wave's operands of one K-step from its LDS stage: per fragment the scale register
-// (byte 0: block h, byte 1: block 2 + h of the lane's row) and the two instructions' code chunks.
-// Fragment and wave row offsets are multiples of 32, so a row's chunk swizzle depends on l32
-// alone: every read is a per-lane base plus an immediate.
-template <class T, class D>
-__device__ __forceinline__ void mx_read(const uint8_t* cur, int wm, int wn, int l32, int h, uint32_t psel,
-                                        uint32_t (&sA)[T::FRAG_M], uint32_t (&sB)[T::FRAG_N],
-                                        i32x4_t (&cA)[2][T::FRAG_M], i32x4_t (&cB)[2][T::FRAG_N]) {
-  const int sw4 = (l32 >> 2) & 3;
-  const int ra = wm * T::FRAG_M * 32 + l32, rb = T::BM + wn * T::FRAG_N * 32 + l32;  // the lane's first rows
-#pragma unroll
-  for (int i = 0; i < T::FRAG_M; ++i) {
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (ra >> 2) * 16 + i * 8 * 16);
-    sA[i] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + ra * 64 + 16 * ((2 * s2 + h) ^ sw4) + i * 32 * 64);
-  }
-#pragma unroll
-  for (int j = 0; j < T::FRAG_N; ++j) {
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (rb >> 2) * 16 + j * 8 * 16);
-    sB[j] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + rb * 64 + 16 * ((2 * s2 + h) ^ sw4) + j * 32 * 64);
-  }
-}
-
-// As mx_read, but the scale dwords are kept as read (two per fragment: blocks h and 2 + h) and
-// combined only where they are used, so that no LDS wait falls between the matrix instructions.
-template <class T, class D>
-__device__ __forceinline__ void mx_read_raw(const uint8_t* cur, int wm, int wn, int l32, int h,
-                                            uint32_t (&qA)[T::FRAG_M][2], uint32_t (&qB)[T::FRAG_N][2],
-                                            i32x4_t (&cA)[2][T::FRAG_M], i32x4_t (&cB)[2][T::FRAG_N]) {
-  const int sw4 = (l32 >> 2) & 3;
-  const int ra = wm * T::FRAG_M * 32 + l32, rb = T::BM + wn * T::FRAG_N * 32 + l32;
-#pragma unroll
-  for (int i = 0; i < T::FRAG_M; ++i) {
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (ra >> 2) * 16 + i * 8 * 16);
-    qA[i][0] = sq[h];
-    qA[i][1] = sq[2 + h];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + ra * 64 + 16 * ((2 * s2 + h) ^ sw4) + i * 32 * 64);
-  }
-#pragma unroll
-  for (int j = 0; j < T::FRAG_N; ++j) {
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (rb >> 2) * 16 + j * 8 * 16);
-    qB[j][0] = sq[h];
-    qB[j][1] = sq[2 + h];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + rb * 64 + 16 * ((2 * s2 + h) ^ sw4) + j * 32 * 64);
-  }
-}
-
-// One K-step on the matrix cores: weights first (output columns n), activations second (output
-// rows m), as in the f16 kernel.
-template <int FM, int FN>
-__device__ __forceinline__ void mx_mma(float16_t (&acc)[FM][FN], const uint32_t (&sA)[FM], const uint32_t (&sB)[FN],
-                                       const i32x4_t (&cA)[2][FM], const i32x4_t (&cB)[2][FN]) {
-  // FP4 operands occupy the first four registers of the instruction's eight
-  auto w = [](i32x4_t c) { return __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1); };
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w(cB[0][j]), w(cA[0][i]), acc[i][j], 4, 4, 0, sB[j], 0,
-                                                                  sA[i]);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w(cB[1][j]), w(cA[1][i]), acc[i][j], 4, 4, 1, sB[j], 1,
-                                                                  sA[i]);
-}
-
-// K-step kt of the register-prefetching loop: operands of kt are in (qA, qB, cA, cB); those of
-// kt + 1 are read into (nA, nB, dA, dB) while kt multiplies.  Once every wave holds K-step kt in
-// registers, its slot `sl` = kt % S is refilled with K-step kt + S.  Past the last K-step the
-// last one is reloaded and re-read, so every step issues the same loads (uniform vmcnt) and
-// runs without branches.  The matrix instructions are interleaved with the LDS reads and the
-// direct loads (one wave per SIMD: nothing else fills the matrix pipe while this wave stalls).
-template <class T, class D, int S>
-__device__ __forceinline__ void mx_pf_step(int kt, int sl, int nkt, uint8_t* lds,
-                                           float16_t (&acc)[T::FRAG_M][T::FRAG_N], int wave, int wm, int wn, int l32,
-                                           int h, uint32_t psel, const uint8_t* const* c_base, const uint32_t* c_off,
-                                           const uint8_t* const* s_base, const uint32_t* s_off,
-                                           const uint32_t* s_stride, const uint32_t (&qA)[T::FRAG_M][2],
-                                           const uint32_t (&qB)[T::FRAG_N][2], const i32x4_t (&cA)[2][T::FRAG_M],
-                                           const i32x4_t (&cB)[2][T::FRAG_N], uint32_t (&nA)[T::FRAG_M][2],
-                                           uint32_t (&nB)[T::FRAG_N][2], i32x4_t (&dA)[2][T::FRAG_M],
-                                           i32x4_t (&dB)[2][T::FRAG_N]) {
-  constexpr int FM = T::FRAG_M, FN = T::FRAG_N;
-  vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step kt + 1 has landed
-  uint32_t sA[FM], sB[FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) sA[i] = __builtin_amdgcn_perm(qA[i][1], qA[i][0], psel);
-#pragma unroll
-  for (int j = 0; j < FN; ++j) sB[j] = __builtin_amdgcn_perm(qB[j][1], qB[j][0], psel);
-  const int kn = min(kt + S, nkt - 1);
-  dma_issue<D>(lds + sl * D::STAGE, wave, (uint32_t)kn * (BK / 2), (size_t)kn * (BK / 32), c_base, c_off, s_base,
-               s_off, s_stride);
-  const int sn = sl == S - 1 ? 0 : sl + 1;
-  mx_read_raw<T, D>(lds + sn * D::STAGE, wm, wn, l32, h, nA, nB, dA, dB);
-  mx_mma(acc, sA, sB, cA, cB);
-  // per matrix instruction of the first 2 (FM + FN): two LDS reads and one direct load
-#pragma unroll
-  for (int g = 0; g < 2 * (FM + FN); ++g) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // vector memory read
-  }
-}
-
-// `ms` is the row stride of the activation scale tensor (M rounded up to 4).  PF selects the
-// register-prefetching K loop (for one wave per SIMD, whose LDS latency no other wave hides).
-template <int WAVES_M, int WAVES_N, int FM, int FN, int S, bool PF, bool LORA>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
-    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
-    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
-    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M, int N, int K, int R, int ms,
-    uint16_t* __restrict__ y) {
-  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
-  using D = DmaTileMx<T, S>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[D::LDS_BYTES];
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: wave-level addresses in scalar registers
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int tiles_n = (N + T::BN - 1) / T::BN;
-  int tm, tn;
-  tile_of((int)blockIdx.x, (int)gridDim.x, (M + T::BM - 1) / T::BM, tiles_n, tm, tn);
-  const int n0 = tn * T::BN;
-  const int m0 = tm * T::BM;
-  const uint32_t kbytes = (uint32_t)K / 2;
-  const int nkt = K / BK;
-  const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);
-  const int srows_a = min(T::BM, ms - m0);  // scale rows: whole quads (ms % 4 == 0, N % 4 == 0)
-
-  const uint8_t* c_base[D::ROUNDS];
-  uint32_t c_off[D::ROUNDS];
-#pragma unroll
-  for (int r = 0; r < D::ROUNDS; ++r) {
-    const int row = r * D::ROUND_ROWS + wave * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ code_swizzle(row);
-    const bool is_a = row < T::BM;
-    const int src = is_a ? min(row, rows_a - 1) : min(row - T::BM, rows_b - 1);
-    c_base[r] = is_a ? qa + (size_t)m0 * kbytes : qw + (size_t)n0 * kbytes;
-    c_off[r] = (uint32_t)src * kbytes + 16u * (uint32_t)c;
-  }
-  // scale dword of each round: LDS dword index d -> quad d / 4 (tile rows 4 quad ..), block d % 4
-  const uint8_t* s_base[D::SROUNDS];
-  uint32_t s_off[D::SROUNDS], s_stride[D::SROUNDS];
-#pragma unroll
-  for (int r = 0; r < D::SROUNDS; ++r) {
-    const int d = min((r * D::WAVES + wave) * 64 + lane, D::SDW - 1);
-    const int quad = d >> 2, g = d & 3;
-    const bool is_a = 4 * quad < T::BM;
-    const int row = is_a ? min(4 * quad, srows_a - 4) : min(4 * quad - T::BM, rows_b - 4);
-    s_base[r] = is_a ? sa + m0 : sw + n0;
-    s_stride[r] = is_a ? (uint32_t)ms : (uint32_t)N;
-    s_off[r] = (uint32_t)g * s_stride[r] + (uint32_t)row;
-  }
-
-  float16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // byte of the lane's row in a scale dword: result byte 0 from the block-h dword, byte 1 from
-  // the block-(2 + h) dword
-  const uint32_t psel = (uint32_t)(l32 & 3) | ((uint32_t)(4 + (l32 & 3)) << 8) | 0x0C0C0000u;
-
-  // K-step kt covers 4 scale blocks: block rows 4 kt .. 4 kt + 3 of the scale tensors.
-  if constexpr (PF) {
-    static_assert((S - 1) * D::LOADS < 64, "vmcnt range");
-    // K-steps 0 .. S - 1 fill every slot up front (the last K-step repeated where there are fewer)
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const int kj = min(j, nkt - 1);
-      dma_issue<D>(lds + j * D::STAGE, wave, (uint32_t)kj * (BK / 2), (size_t)kj * (BK / 32), c_base, c_off, s_base,
-                   s_off, s_stride);
-    }
-    vm_wait_barrier<(S - 1) * D::LOADS>();  // K-step 0 has landed
-    uint32_t sA0[FM][2], sB0[FN][2], sA1[FM][2], sB1[FN][2];
-    i32x4_t cA0[2][FM], cB0[2][FN], cA1[2][FM], cB1[2][FN];
-    mx_read_raw<T, D>(lds, wm, wn, l32, h, sA0, sB0, cA0, cB0);
-    int kt = 0, sl = 0;
-    for (; kt + 1 < nkt; kt += 2) {
-      mx_pf_step<T, D, S>(kt, sl, nkt, lds, acc, wave, wm, wn, l32, h, psel, c_base, c_off, s_base, s_off, s_stride,
-                          sA0, sB0, cA0, cB0, sA1, sB1, cA1, cB1);
-      sl = sl == S - 1 ? 0 : sl + 1;
-      mx_pf_step<T, D, S>(kt + 1, sl, nkt, lds, acc, wave, wm, wn, l32, h, psel, c_base, c_off, s_base, s_off,
-                          s_stride, sA1, sB1, cA1, cB1, sA0, sB0, cA0, cB0);
-      sl = sl == S - 1 ? 0 : sl + 1;
-    }
-    if (kt < nkt)
-      mx_pf_step<T, D, S>(kt, sl, nkt, lds, acc, wave, wm, wn, l32, h, psel, c_base, c_off, s_base, s_off, s_stride,
-                          sA0, sB0, cA0, cB0, sA1, sB1, cA1, cB1);
-    vm_wait_barrier<0>();
-    epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, y);
-    return;
-  }
-
-  // The first S - 1 K-steps are issued up front (past the last one, the last is reloaded).
-#pragma unroll
-  for (int j = 0; j < S - 1; ++j) {
-    const int kj = min(j, nkt - 1);
-    dma_issue<D>(lds + j * D::STAGE, wave, (uint32_t)kj * (BK / 2), (size_t)kj * (BK / 32), c_base, c_off, s_base,
-                 s_off, s_stride);
-  }
-  vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step 0 has landed
-  int slot = 0;
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int slot2 = slot == 0 ? S - 1 : slot - 1;  // (kt + S - 1) % S: read in K-step kt - 1, now free
-    const int kn = min(kt + S - 1, nkt - 1);
-    dma_issue<D>(lds + slot2 * D::STAGE, wave, (uint32_t)kn * (BK / 2), (size_t)kn * (BK / 32), c_base, c_off, s_base,
-                 s_off, s_stride);
-    uint32_t sA[FM], sB[FN];
-    i32x4_t cA[2][FM], cB[2][FN];
-    mx_read<T, D>(lds + slot * D::STAGE, wm, wn, l32, h, psel, sA, sB, cA, cB);
-    mx_mma(acc, sA, sB, cA, cB);
-    vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step kt + 1 has landed
-    slot = slot == S - 1 ? 0 : slot + 1;
-  }
-  vm_wait_barrier<0>();
-
-  epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, y);
-}
-
-template <int WAVES_M, int WAVES_N, int FM, int FN, int S = 3, bool PF = false>
-hipError_t launch_mx_tile(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
-                          const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
-                          const uint16_t* wts, const uint16_t* bias, int M, int N, int K, int R, int ms, uint16_t* y) {
-  using T = Tile<WAVES_M, WAVES_N, FM, FN>;
-  dim3 grid((unsigned)(((N + T::BN - 1) / T::BN) * ((M + T::BM - 1) / T::BM)));
-  dim3 block(T::THREADS);
-  if (rb > 0)
-    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, PF, true><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, ms, y);
-  else
-    gemm_mx_kernel<WAVES_M, WAVES_N, FM, FN, S, PF, false><<<grid, block, 0, st>>>(qa, sa, lora, parts, qw, sw, pu, wcs, wts, bias, M, N, K, R, ms, y);
-  return hipGetLastError();
-}
-
 template <int WAVES_M, int WAVES_N, int FM, int FN, bool VEC16>
 hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                      const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs,
@@ -1352,19 +597,6 @@ hipError_t launch_rb(int rb, hipStream_t st, const uint8_t* qa, const uint8_t* s
   }
 #undef W4A4_GEMM_GO
   return hipGetLastError();
-}
-
-// Compute units of the current device (cached per device; concurrent first calls store the same value).
-int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 // Workgroups of the persistent kernel with this tile: as many as run at once (resident
@@ -1509,39 +741,6 @@ hipError_t launch_gemm(const void* qact, const void* ascales, const float* lora,
       return launch_tile<4, 2, 2, 3>(dma, rb, vec16, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
   }
 #undef W4A4_TILE_CASE
-}
-
-hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lora, int lora_parts,
-                          const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
-                          const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
-                          int64_t ms, void* y, hipStream_t stream) {
-  const int rb = (int)((R + 15) / 16);
-  auto qa = static_cast<const uint8_t*>(qact);
-  auto sa = static_cast<const uint8_t*>(ascales);
-  auto qw = static_cast<const uint8_t*>(qweight);
-  auto sw = static_cast<const uint8_t*>(wscales);
-  auto pu = static_cast<const uint16_t*>(proj_up);
-  auto wc = static_cast<const uint16_t*>(wcscales);
-  auto wt = static_cast<const uint16_t*>(wtscale);
-  auto bs = static_cast<const uint16_t*>(bias);
-  auto yp = static_cast<uint16_t*>(y);
-  const int m = (int)M, n = (int)N, k = (int)K, r = (int)R, s = (int)ms;
-  // 16-wave 256 x 256 tiles (each wave 64 x 64: four waves per SIMD hide each other's scale
-  // permutes, LDS reads and barrier waits) unless 4-wave 128 x 128 tiles need fewer rounds of
-  // 256 tiles by more than the measured per-tile time ratio (2.4: 41 vs 17 us at K = 3072);
-  // W4A4_GEMM_TILE=4x4x2x2, 2x4x4x2 (8 waves of 128 x 64), 2x2x4x4 (4 waves of 128 x 128 with
-  // register prefetch: half the LDS reads, but measured slower) or 2x2x2x2 forces one
-  const char* forced = test_hook("W4A4_GEMM_TILE");
-  const int64_t rounds256 = ((M + 255) / 256 * ((N + 255) / 256) + 255) / 256;
-  const int64_t rounds128 = ((M + 127) / 128 * ((N + 127) / 128) + 255) / 256;
-  const bool big = forced ? !strcmp(forced, "4x4x2x2") : 2.4 * (double)rounds256 <= (double)rounds128;
-  if (forced && !strcmp(forced, "2x2x4x4"))
-    return launch_mx_tile<2, 2, 4, 4, 3, true>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s,
-                                               yp);
-  if (forced && !strcmp(forced, "2x4x4x2"))
-    return launch_mx_tile<2, 4, 4, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s, yp);
-  if (big) return launch_mx_tile<4, 4, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s, yp);
-  return launch_mx_tile<2, 2, 2, 2>(rb, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s, yp);
 }
 
 }  // namespace w4a4

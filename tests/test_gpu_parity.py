@@ -150,7 +150,8 @@ def test_gemm_lowrank_parity(w4, M, N, K, R):
 
 @pytest.mark.parametrize("path", ["wide", "stream", "regs"])
 @pytest.mark.parametrize("M,N,K,R", [(16, 600, 5120, 32), (1, 64, 512, 8), (13, 36, 8192, 64), (16, 100, 1024, 0),
-                                     (8, 200, 2560, 16), (12, 68, 3584, 32), (4, 40, 512, 64), (16, 130, 1024, 33)])
+                                     (8, 200, 2560, 16), (12, 68, 3584, 32), (4, 40, 512, 64), (16, 130, 1024, 33),
+                                     (16, 13824, 5120, 32), (16, 16000, 3072, 64), (16, 4, 128, 1), (16, 1028, 640, 8)])
 def test_skinny_paths(w4, M, N, K, R, path, hooks):
     """Each weight-streaming kernel (64-row wide, 32-row LDS-staged, registers-only), forced
     through W4A4_SKINNY_PATH; shapes a variant does not accept fall back to the next one."""

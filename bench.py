@@ -130,19 +130,19 @@ def sleep_cycles(torch, stream, seconds):
     return int(min(seconds / per_cycle, 1 << 31))
 
 
-def shader_clock_mhz(torch, stream):
-    """The shader clock now, from a spin kernel of 2^20 clock cycles timed with HIP events (MHz)."""
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    torch.cuda._sleep(1 << 20)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return round((1 << 20) / max(e0.elapsed_time(e1) * 1e-3, 1e-9) / 1e6, 1)
+def smi_state(flags):
+    """rocm-smi's fields for the given query flags (power, performance level, clocks), or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi"] + flags + ["--json"], capture_output=True, text=True, timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        return {k: v for k, v in card.items() if any(w in k.lower() for w in ("power", "perf", "sclk", "mclk", "fclk"))}
+    except Exception:  # pragma: no cover - tool missing or unparsable output
+        return None
 
 
 def run_environment(torch):
     """ROCm version, GPU, and the power state rocm-smi reports (None where unavailable)."""
-    import subprocess
     props = torch.cuda.get_device_properties(0)
     env = {"rocm": None, "gpu": getattr(props, "gcnArchName", props.name), "cus": props.multi_processor_count,
            "torch": torch.__version__, "power": None}
@@ -151,14 +151,7 @@ def run_environment(torch):
             env["rocm"] = f.read().strip()
     except OSError:
         pass
-    try:
-        out = subprocess.run(["rocm-smi", "--showpower", "--showperflevel", "--showmaxpower", "--showclocks",
-                              "--json"], capture_output=True, text=True, timeout=20).stdout
-        card = next(iter(json.loads(out).values()))
-        env["power"] = {k: v for k, v in card.items()
-                        if any(w in k.lower() for w in ("power", "perf", "sclk", "mclk", "fclk"))}
-    except Exception:  # pragma: no cover - tool missing or unparsable output
-        pass
+    env["power"] = smi_state(["--showpower", "--showperflevel", "--showmaxpower", "--showclocks"])
     return env
 
 
@@ -367,8 +360,8 @@ def main():
     wall_ms = (t1 - t0) * 1e3 / args.steps
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # the shader clock right after the timed steps (a spin kernel of known cycle count)
-    sclk_after = shader_clock_mhz(torch, stream)
+    # rocm-smi's power and clock state right after the timed steps
+    smi_after = smi_state(["--showpower", "--showclocks"])
 
     # Per-kernel durations: the same two kernels through the two-entry-point form, each launched
     # back to back (one HIP event pair around the whole run of launches: a pair around every
@@ -468,7 +461,7 @@ def main():
                    "hadamard_block": B, "input_sets": nsets, "graph": bool(args.graph)},
         "frac_of_fp4_peak": round(value / PEAK_FP4_MFMA_TFLOPS, 4),
         "layer": layer, "kernels": kernels, "roofline": roof, "cpu_baseline": cpu,
-        "env": dict(env, sclk_mhz_after_timed=sclk_after),
+        "env": dict(env, power_after_timed=smi_after),
     }
     print(json.dumps(line), flush=True)
 

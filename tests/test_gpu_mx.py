@@ -125,6 +125,35 @@ def test_gemm_mx_each_tile(w4, tile, N, hooks):
     _check_gemm_mx(w4, _lay(300, 640, N, 32, 0, seed=41))
 
 
+@pytest.mark.parametrize("M,N,K,R", [(16, 13824, 5120, 32), (1, 64, 512, 32), (5, 300, 1024, 8), (16, 1000, 3072, 64),
+                                     (7, 132, 2560, 0), (16, 8196, 5120, 16), (13, 68, 4608, 33), (3, 4, 512, 1)])
+def test_gemm_mx_weight_streaming(w4, M, N, K, R, hooks):
+    """Batches of at most 16 rows with K a multiple of 512 up to 5120 stream the weights through the
+    scaled 16x16x128 FP4 instruction (K = 5120 specialised, ragged N, every rank form): against
+    the oracle, and against the tiled kernel (W4A4_SKINNY_PATH=tiled) within the same gates."""
+    lay = _lay(M, K, N, R, 0, seed=M * 11 + N)
+    y_stream = _check_gemm_mx(w4, lay)
+    hooks.setenv("W4A4_SKINNY_PATH", "tiled")
+    y_tiled = _check_gemm_mx(w4, lay)
+    H.assert_gates(y_stream, y_tiled, "streaming vs tiled MX GEMM")
+
+
+@pytest.mark.parametrize("M,N,K,R,B", [(16, 2048, 5120, 32, 32), (4, 640, 1024, 16, 0)])
+def test_linear_mx_small_batch(w4, M, N, K, R, B):
+    """The MX layer at small batches: the K-split quantizer's partial low-rank sums meet in the
+    weight-streaming GEMM's epilogue."""
+    import torch
+    lay = _lay(M, K, N, R, B, seed=M + K)
+    qw, sw = _mx_weights(lay)
+    y = w4.svdq_linear_mx(H.to_dev_bf16(lay["x"]), H.device_layer(lay, qw, sw), hadamard_block=B)
+    torch.cuda.synchronize()
+    f = synth.as_f32(lay)
+    layer = dict(qweight=qw, wscales=sw, proj_down=f["proj_down"], proj_up=f["proj_up"],
+                 smooth_factor=f["smooth_factor"], wcscales=f["wcscales"], wtscale=f["wtscale"])
+    _, y_ref, _ = omx.svdq_linear_mx(f["x"], layer, B)
+    H.assert_gates(H.from_dev_bf16_f64(y), y_ref, "svdq_linear_mx small batch")
+
+
 @pytest.mark.parametrize("tile", ["4x4x2x2", "2x2x4x4"])
 @pytest.mark.parametrize("K", [128, 256, 384])
 def test_gemm_mx_few_k_steps(w4, tile, K, hooks):

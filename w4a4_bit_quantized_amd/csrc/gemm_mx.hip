@@ -307,6 +307,11 @@ hipError_t launch_gemm_mx(const void* qact, const void* ascales, const float* lo
   auto bs = static_cast<const uint16_t*>(bias);
   auto yp = static_cast<uint16_t*>(y);
   const int m = (int)M, n = (int)N, k = (int)K, r = (int)R, s = (int)ms;
+  // batches of at most 16 rows stream the weights (W4A4_SKINNY_PATH=tiled keeps the tiles)
+  const char* sp = test_hook("W4A4_SKINNY_PATH");
+  if (!(sp && !strcmp(sp, "tiled")) && skinny_mx_supported(M, K, R, lora_parts))
+    return launch_gemm_skinny_mx(qact, ascales, lora, lora_parts, qweight, wscales, proj_up, wcscales, wtscale, bias, M,
+                                 N, K, R, ms, y, stream);
   // 16-wave 256 x 256 tiles (each wave 64 x 64: four waves per SIMD hide each other's scale
   // permutes, LDS reads and barrier waits) unless 4-wave 128 x 128 tiles need fewer rounds of
   // 256 tiles by more than the measured per-tile time ratio (2.4: 41 vs 17 us at K = 3072);

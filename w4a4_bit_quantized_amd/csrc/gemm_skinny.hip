@@ -587,6 +587,173 @@ __global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_wide_kernel(
   if (m < M && n0 + n < N) y[(size_t)m * N + n0 + n] = (uint16_t)f32_to_bf16_bits(v);
 }
 
+// ---- MXFP4 wide variant (M <= 16, K <= 5120 a multiple of 512) ------------------------------
+// The wide kernel's streaming with the MX formats (rotate notes, section 3.3: FP-Quant mxfp4): one
+// E8M0 scale per 32 K-columns, activation scales (K/32, ms) with ms = M rounded up to 4, weight
+// scales (K/32, N).  Per chunk of 512 K-columns thread t loads 16 bytes of weight row t / 16, 4
+// bytes of activation row t / 64, the wscales byte of block row t / 64 and column t % 64, and
+// (t < 256) the ascales byte of block row t / 16 and row t % 16.  The product runs on
+// v_mfma_scale_f32_16x16x128_f8f6f4, which takes the packed E2M1 codes and the E8M0 bytes
+// directly: wave w multiplies weight block w % 4 (16 rows) by the 16 activation rows over the
+// chunk's K-columns 128 (w / 4) .. +128, lane (i = lane % 16, kq = lane / 16) supplying 16 code
+// bytes (32 columns, one scale block) of weight row 16 (w % 4) + i and of activation row i, and
+// the two blocks' scale bytes.  The four waves of each weight block meet in LDS in a fixed order;
+// the epilogue is the nvfp4 wide kernel's.
+constexpr int SX_W = 0;                              // slot: weight rows (SS_ROW bytes each)
+constexpr int SX_A = SX_W + SW_BN * SS_ROW;          //       activation rows
+constexpr int SX_S = SX_A + 16 * SS_ROW;             //       wscales [16 blocks][64 columns]
+constexpr int SX_AS = SX_S + 16 * SW_BN;             //       ascales [16 blocks][16 rows]
+constexpr int SX_SLOT = SX_AS + 16 * 16;
+constexpr int SX_REDB = (4 + 1) * 16 * SW_RED * 4;   // four K-step partials and the rank-R term
+constexpr int SX_EPI = 2 * SX_SLOT > SX_REDB ? 2 * SX_SLOT : SX_REDB;
+constexpr int SX_LHI = SX_EPI;
+constexpr int SX_LLO = SX_LHI + 16 * SW_RS * 2;
+constexpr int SX_P = SX_LLO + 16 * SW_RS * 2;
+constexpr int SX_C = SX_P + SW_BN * SW_RS * 2;
+constexpr int SX_TRASH = SX_C + SW_BN * 4;
+constexpr int SX_LDS = SX_TRASH + 16;
+static_assert(SX_LDS <= 160 * 1024, "LDS of one CU");
+
+template <bool LORA, int RP, bool FULL>
+__global__ __launch_bounds__(64 * SW_WAVES) void gemm_skinny_mx_kernel(
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const float* __restrict__ lora, int parts,
+    const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw, const uint16_t* __restrict__ pu,
+    const uint16_t* __restrict__ wcs, const uint16_t* __restrict__ wts, const uint16_t* __restrict__ bias, int M,
+    int N, int K, int R, int ms, uint16_t* __restrict__ y) {
+  static_assert(!LORA || RP == 32 || RP == 64, "rank padded to one or two MFMA steps");
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SX_LDS];
+  uint16_t* l_hi = reinterpret_cast<uint16_t*>(smem + SX_LHI);
+  uint16_t* l_lo = reinterpret_cast<uint16_t*>(smem + SX_LLO);
+  uint16_t* p_lds = reinterpret_cast<uint16_t*>(smem + SX_P);
+  float* c_lds = reinterpret_cast<float*>(smem + SX_C);
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int blk = wave & 3, ks = wave >> 2;  // the wave's weight block and K-step within a chunk
+  const int n0 = xcd_tile(blockIdx.x, gridDim.x) * SW_BN;
+  const int kbytes = K / 2;
+  const int nc = FULL ? SS_MAXC : kbytes / SS_CH;  // 1 .. SS_MAXC
+
+  // ---- epilogue operands first: the oldest loads, complete before the first chunk is used ----
+  constexpr int RPP = RP > 0 ? RP : 1;
+  constexpr int PPT = LORA ? SW_BN * RP / (64 * SW_WAVES) : 1;
+  const uint32_t cval = wcs[min(n0 + (t & 63), N - 1)];
+  const uint32_t tsv = wts[0];
+  const int lm = t / RPP, lr = t % RPP;  // the (m, r) element of L this thread stages
+  float lv[SS_MAXPARTS];
+  uint32_t pval[PPT];
+  if (LORA) {
+    const int at = min(min(lm, M - 1) * R + min(lr, R - 1), M * R - 1);
+#pragma unroll
+    for (int p = 0; p < SS_MAXPARTS; ++p) lv[p] = lora[(size_t)min(p, parts - 1) * M * R + at];
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = t + u * 64 * SW_WAVES;
+      pval[u] = pu[(size_t)min(n0 + i / RPP, N - 1) * R + min(i % RPP, R - 1)];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint8_t* wsrc = qw + (size_t)min(n0 + (t >> 4), N - 1) * kbytes + 16 * (t & 15);
+  const uint8_t* asrc = qa + (size_t)min(t >> 6, M - 1) * kbytes + 4 * (t & 63);
+  const uint32_t soff = (uint32_t)((t >> 6) * N + min(n0 + (t & 63), N - 1));       // within a chunk's blocks
+  const uint32_t asoff = (uint32_t)((((t & 255) >> 4) * ms) + min(t & 15, M - 1));
+  u32x4_t wr[SS_MAXC];
+  uint32_t ar[SS_MAXC], sr[SS_MAXC], asr[SS_MAXC];
+#define W4A4_SX_ISSUE(j)                                                              \
+  do {                                                                                \
+    const int c_ = FULL ? (j) : min((j), nc - 1);                                     \
+    wr[(j)] = *reinterpret_cast<const u32x4_t*>(wsrc + c_ * SS_CH);                   \
+    ar[(j)] = *reinterpret_cast<const uint32_t*>(asrc + c_ * SS_CH);                  \
+    sr[(j)] = (sw + (size_t)c_ * 16 * N)[soff];                                       \
+    asr[(j)] = (sa + (size_t)c_ * 16 * ms)[asoff];                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+  } while (0)
+#pragma unroll
+  for (int j = 0; j < SW_AHEAD; ++j) W4A4_SX_ISSUE(j);
+
+  c_lds[t & 63] = bf16_bits_to_f32(cval) * bf16_bits_to_f32(tsv);  // repeated lanes store the same value
+  if (LORA) {
+    // L[m, r] = sum of the parts in order (zero outside M x R), as bf16 hi + lo
+    float sum = 0.0f;
+#pragma unroll
+    for (int p = 0; p < SS_MAXPARTS; ++p) sum += p < parts ? lv[p] : 0.0f;
+    sum = (lm < M && lr < R) ? sum : 0.0f;
+    const uint32_t hb = f32_to_bf16_bits(sum);
+    const uint32_t lb = f32_to_bf16_bits(sum - bf16_bits_to_f32(hb));  // exact remainder, rounded
+    const bool staged = t < 16 * RP;
+    *(staged ? l_hi + lm * SW_RS + lr : reinterpret_cast<uint16_t*>(smem + SX_TRASH)) = (uint16_t)hb;
+    *(staged ? l_lo + lm * SW_RS + lr : reinterpret_cast<uint16_t*>(smem + SX_TRASH + 2)) = (uint16_t)lb;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = t + u * 64 * SW_WAVES;
+      p_lds[(i / RPP) * SW_RS + i % RPP] = (i % RPP) < R ? (uint16_t)pval[u] : (uint16_t)0;
+    }
+  }
+
+  float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+  const int kb = 64 * ks + 16 * kq;  // byte of the lane's 32 codes within a chunk row
+  const int sb = 4 * ks + kq;        // their scale block within the chunk
+  uint8_t* const wdst = smem + SX_W + (t >> 4) * SS_ROW + 16 * (t & 15);
+  uint8_t* const adst = smem + SX_A + (t >> 6) * SS_ROW + 4 * (t & 63);
+  uint8_t* const sdst = smem + SX_S + t;                 // [block t / 64][column t % 64]
+  uint8_t* const asdst = smem + SX_AS + (t & 255);       // [block][row]
+  const uint8_t* const w_op = smem + SX_W + (16 * blk + r16) * SS_ROW + kb;
+  const uint8_t* const a_op = smem + SX_A + r16 * SS_ROW + kb;
+  const uint8_t* const ws_op = smem + SX_S + sb * SW_BN + 16 * blk + r16;
+  const uint8_t* const as_op = smem + SX_AS + sb * 16 + r16;
+#pragma unroll
+  for (int i = 0; i < SS_MAXC; ++i) {
+    if (i + SW_AHEAD < SS_MAXC) W4A4_SX_ISSUE(i + SW_AHEAD);
+    // every chunk is staged, also past the last one, so the loads stay where they were issued
+    const int so = (i & 1) * SX_SLOT;
+    *reinterpret_cast<u32x4_t*>(wdst + so) = wr[i];
+    *reinterpret_cast<uint32_t*>(adst + so) = ar[i];
+    sdst[so] = (uint8_t)sr[i];
+    if (t < 256) asdst[so] = (uint8_t)asr[i];
+    lds_barrier();  // also: every wave is done with the chunk this slot held two steps ago
+    if (!FULL && i >= nc) continue;  // workgroup-uniform
+    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(w_op + so);
+    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(a_op + so);
+    const int wsc = ws_op[so], asc = as_op[so];
+    // FP4 operands occupy the first four registers of the instruction's eight
+    const i32x4_t w4 = __builtin_bit_cast(i32x4_t, wv), a4 = __builtin_bit_cast(i32x4_t, av);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_shufflevector(w4, w4, 0, 1, 2, 3, -1, -1, -1, -1),
+                                                          __builtin_shufflevector(a4, a4, 0, 1, 2, 3, -1, -1, -1, -1), acc,
+                                                          4, 4, 0, wsc, 0, asc);
+  }
+#undef W4A4_SX_ISSUE
+  lds_barrier();  // the slots are free: the reduction reuses them
+
+  // partials -> LDS: lane holds m = lane % 16, n = 16 blk + 4 kq + e of K-step ks; rows 4 * 16 ..
+  // hold the rank-R term (waves 0..3, one 16-column block each)
+  float* red = reinterpret_cast<float*>(smem);
+  *reinterpret_cast<float4_t*>(red + (ks * 16 + r16) * SW_RED + 16 * blk + 4 * kq) = acc;
+  if (LORA && wave < 4) {
+    float4_t la = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r0 = 0; r0 < RP; r0 += 32) {
+      const bf16x8_t pv = *reinterpret_cast<const bf16x8_t*>(p_lds + (16 * wave + r16) * SW_RS + r0 + 8 * kq);
+      const bf16x8_t lh = *reinterpret_cast<const bf16x8_t*>(l_hi + r16 * SW_RS + r0 + 8 * kq);
+      const bf16x8_t ll = *reinterpret_cast<const bf16x8_t*>(l_lo + r16 * SW_RS + r0 + 8 * kq);
+      la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv, lh, la, 0, 0, 0);
+      la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv, ll, la, 0, 0, 0);
+    }
+    *reinterpret_cast<float4_t*>(red + (4 * 16 + r16) * SW_RED + 16 * wave + 4 * kq) = la;
+  }
+  lds_barrier();
+  const int m = t >> 6, n = t & 63;
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) s += red[(w * 16 + m) * SW_RED + n];
+  float v = s * c_lds[n];
+  if (LORA) v += red[(4 * 16 + m) * SW_RED + n];
+  if (bias != nullptr) v += bf16_bits_to_f32(bias[min(n0 + n, N - 1)]);
+  if (m < M && n0 + n < N) y[(size_t)m * N + n0 + n] = (uint16_t)f32_to_bf16_bits(v);
+}
+
 template <int MB, bool VEC16>
 hipError_t launch_mb(bool lora_on, hipStream_t st, const uint8_t* qa, const uint8_t* sa, const float* lora, int parts,
                      const uint8_t* qw, const uint8_t* sw, const uint16_t* pu, const uint16_t* wcs, const uint16_t* wts,
@@ -656,6 +823,41 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
   }
   if (vec16) return launch_mb<2, true>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
   return launch_mb<2, false>(lo, stream, qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, yp);
+}
+
+bool skinny_mx_supported(int64_t M, int64_t K, int64_t R, int lora_parts) {
+  return M >= 1 && M <= 16 && K % (2 * SS_CH) == 0 && K <= 2 * SS_CH * SS_MAXC && R <= 64 && lora_parts >= 1 &&
+         lora_parts <= SS_MAXPARTS;
+}
+
+hipError_t launch_gemm_skinny_mx(const void* qact, const void* ascales, const float* lora, int lora_parts,
+                                 const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
+                                 const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                                 int64_t ms, void* y, hipStream_t stream) {
+  if (!skinny_mx_supported(M, K, R, lora_parts)) return hipErrorInvalidValue;
+  auto qa = static_cast<const uint8_t*>(qact);
+  auto sa = static_cast<const uint8_t*>(ascales);
+  auto qw = static_cast<const uint8_t*>(qweight);
+  auto sw = static_cast<const uint8_t*>(wscales);
+  auto pu = static_cast<const uint16_t*>(proj_up);
+  auto wc = static_cast<const uint16_t*>(wcscales);
+  auto wt = static_cast<const uint16_t*>(wtscale);
+  auto bs = static_cast<const uint16_t*>(bias);
+  auto yp = static_cast<uint16_t*>(y);
+  const int m = (int)M, n = (int)N, k = (int)K, r = (int)R, s = (int)ms;
+  dim3 grid((unsigned)((N + SW_BN - 1) / SW_BN)), block(64 * SW_WAVES);
+  const bool full = K == 2 * SS_CH * SS_MAXC;
+#define W4A4_SX_LAUNCH(LO, RP, FU) \
+  gemm_skinny_mx_kernel<LO, RP, FU><<<grid, block, 0, stream>>>(qa, sa, lora, lora_parts, qw, sw, pu, wc, wt, bs, m, n, k, r, s, yp)
+  if (R == 0) {
+    if (full) W4A4_SX_LAUNCH(false, 0, true); else W4A4_SX_LAUNCH(false, 0, false);
+  } else if (R <= 32) {
+    if (full) W4A4_SX_LAUNCH(true, 32, true); else W4A4_SX_LAUNCH(true, 32, false);
+  } else {
+    if (full) W4A4_SX_LAUNCH(true, 64, true); else W4A4_SX_LAUNCH(true, 64, false);
+  }
+#undef W4A4_SX_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace w4a4

@@ -54,6 +54,14 @@ hipError_t launch_gemm_skinny(const void* qact, const void* ascales, const float
                               const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
                               void* y, hipStream_t stream);
 
+// MXFP4 weight-streaming variant for M <= 16, K <= 5120 a multiple of 512, R <= 64, at most 8
+// low-rank parts (called by launch_gemm_mx; `ms` is the activation scale row stride).
+bool skinny_mx_supported(int64_t M, int64_t K, int64_t R, int lora_parts);
+hipError_t launch_gemm_skinny_mx(const void* qact, const void* ascales, const float* lora, int lora_parts,
+                                 const void* qweight, const void* wscales, const void* proj_up, const void* wcscales,
+                                 const void* wtscale, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                                 int64_t ms, void* y, hipStream_t stream);
+
 // Standalone block Hadamard transform of rows x cols elements (row strides ldx, ldy in
 // elements; dtype 0 bf16, 1 f16, 2 f32; block a power of two in [2, 4096] dividing cols);
 // norm = float32(1 / sqrt(block)).  x == y (with ldx == ldy) transforms in place.

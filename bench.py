@@ -61,6 +61,8 @@ KERNEL_SOURCES = {
     "gemm_skinny": ["w4a4_bit_quantized_amd/csrc/gemm_skinny.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "gemm_mx": ["w4a4_bit_quantized_amd/csrc/gemm_mx.hip", "w4a4_bit_quantized_amd/csrc/gemm_common.h",
                 "w4a4_bit_quantized_amd/csrc/device_common.h"],
+    "gemm_skinny_mx": ["w4a4_bit_quantized_amd/csrc/gemm_skinny.hip", "w4a4_bit_quantized_amd/csrc/gemm_mx.hip",
+                       "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "hadamard": ["w4a4_bit_quantized_amd/csrc/hadamard.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
     "quantize": ["w4a4_bit_quantized_amd/csrc/quantize.hip", "w4a4_bit_quantized_amd/csrc/device_common.h"],
 }
@@ -434,7 +436,10 @@ def main():
         ach = g_bytes / (g_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": "gemm_lowrank"}
-    gemm_kernel = "gemm_mx" if args.mx else ("gemm_skinny" if M <= 32 else "gemm")
+    if args.mx:
+        gemm_kernel = "gemm_skinny_mx" if M <= 16 and K % 512 == 0 and K <= 5120 and R <= 64 else "gemm_mx"
+    else:
+        gemm_kernel = "gemm_skinny" if M <= 32 else "gemm"
     roof["kernel"] = gemm_kernel
     tr = traffic_from_profile(gemm_kernel, args.workload)
     roof["traffic"] = None if tr is None else round(tr)

@@ -7,8 +7,11 @@
  * NULL is the default stream).  No entry point allocates, frees or
  * synchronizes.  Validation happens before any launch: a call that returns an
  * error has launched nothing and written nothing.  Faults during execution
- * surface at the caller's next synchronization.  Calls are thread-safe; the
- * library keeps no state between calls.  Checks run in this order: sizes
+ * surface at the caller's next synchronization.  Calls are thread-safe (for
+ * svdq_linear_noalloc see its note on overlapping calls); no call depends on an
+ * earlier one.  The library caches, once per device and atomically, the CU count,
+ * the occupancy of its persistent kernels and the address of the static buffer
+ * of svdq_linear_noalloc.  Checks run in this order: sizes
  * (W4A4_ERR_SHAPE / W4A4_ERR_UNSUPPORTED), the empty call (M or N == 0 is
  * valid, launches nothing and may pass NULL pointers), NULL pointers
  * (W4A4_ERR_NULL), alignment (W4A4_ERR_ALIGN).

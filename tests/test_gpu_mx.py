@@ -138,6 +138,17 @@ def test_gemm_mx_weight_streaming(w4, M, N, K, R, hooks):
     H.assert_gates(y_stream, y_tiled, "streaming vs tiled MX GEMM")
 
 
+@pytest.mark.parametrize("M,N,K,R", [(16, 1028, 5120, 32), (2, 260, 1536, 0)])
+def test_gemm_mx_weight_streaming_bias(w4, M, N, K, R, hooks):
+    """The bias through the weight-streaming MX GEMM (added after the low-rank term, before the
+    single rounding), against the oracle and the tiled kernel."""
+    lay = _lay(M, K, N, R, 0, seed=N + R)
+    y_stream = _check_gemm_mx(w4, lay, bias=True)
+    hooks.setenv("W4A4_SKINNY_PATH", "tiled")
+    y_tiled = _check_gemm_mx(w4, lay, bias=True)
+    H.assert_gates(y_stream, y_tiled, "streaming vs tiled MX GEMM with bias")
+
+
 @pytest.mark.parametrize("M,N,K,R,B", [(16, 2048, 5120, 32, 32), (4, 640, 1024, 16, 0)])
 def test_linear_mx_small_batch(w4, M, N, K, R, B):
     """The MX layer at small batches: the K-split quantizer's partial low-rank sums meet in the

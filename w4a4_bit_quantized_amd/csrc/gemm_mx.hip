@@ -40,36 +40,10 @@ struct DmaTileMx {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// Read a wave's operands of one K-step from its LDS stage: per fragment the scale register
-// (byte 0: block h, byte 1: block 2 + h of the lane's row) and the two instructions' code chunks.
-// Fragment and wave row offsets are multiples of 32, so a row's chunk swizzle depends on l32
-// alone: every read is a per-lane base plus an immediate.
-template <class T, class D>
-__device__ __forceinline__ void mx_read(const uint8_t* cur, int wm, int wn, int l32, int h, uint32_t psel,
-                                        uint32_t (&sA)[T::FRAG_M], uint32_t (&sB)[T::FRAG_N],
-                                        i32x4_t (&cA)[2][T::FRAG_M], i32x4_t (&cB)[2][T::FRAG_N]) {
-  const int sw4 = (l32 >> 2) & 3;
-  const int ra = wm * T::FRAG_M * 32 + l32, rb = T::BM + wn * T::FRAG_N * 32 + l32;  // the lane's first rows
-#pragma unroll
-  for (int i = 0; i < T::FRAG_M; ++i) {
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (ra >> 2) * 16 + i * 8 * 16);
-    sA[i] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      cA[s2][i] = *reinterpret_cast<const i32x4_t*>(cur + ra * 64 + 16 * ((2 * s2 + h) ^ sw4) + i * 32 * 64);
-  }
-#pragma unroll
-  for (int j = 0; j < T::FRAG_N; ++j) {
-    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (rb >> 2) * 16 + j * 8 * 16);
-    sB[j] = __builtin_amdgcn_perm(sq[2 + h], sq[h], psel);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      cB[s2][j] = *reinterpret_cast<const i32x4_t*>(cur + rb * 64 + 16 * ((2 * s2 + h) ^ sw4) + j * 32 * 64);
-  }
-}
-
-// As mx_read, but the scale dwords are kept as read (two per fragment: blocks h and 2 + h) and
-// combined only where they are used, so that no LDS wait falls between the matrix instructions.
+// Read a wave's operands of one K-step from its LDS stage, the scale dwords as read (two per
+// fragment: blocks h and 2 + h), combined only where they are used.  Fragment and wave row offsets
+// are multiples of 32, so a row's chunk swizzle depends on l32 alone: every read is a per-lane base
+// plus an immediate.
 template <class T, class D>
 __device__ __forceinline__ void mx_read_raw(const uint8_t* cur, int wm, int wn, int l32, int h,
                                             uint32_t (&qA)[T::FRAG_M][2], uint32_t (&qB)[T::FRAG_N][2],
@@ -114,6 +88,52 @@ __device__ __forceinline__ void mx_mma(float16_t (&acc)[FM][FN], const uint32_t 
 #pragma unroll
     for (int j = 0; j < FN; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w(cB[1][j]), w(cA[1][i]), acc[i][j], 4, 4, 1, sB[j], 1,
+                                                                  sA[i]);
+}
+
+// Half-step pieces of the interleaved loop: the code chunks of instruction s2 of every fragment, the
+// raw scale dwords (blocks h and 2 + h) of every fragment, and the matrix instructions of one half.
+template <class T, class D>
+__device__ __forceinline__ void mx_read_codes(const uint8_t* cur, int wm, int wn, int l32, int h, int s2,
+                                              i32x4_t (&cA)[T::FRAG_M], i32x4_t (&cB)[T::FRAG_N]) {
+  const int sw4 = (l32 >> 2) & 3;
+  const int ra = wm * T::FRAG_M * 32 + l32, rb = T::BM + wn * T::FRAG_N * 32 + l32;
+#pragma unroll
+  for (int i = 0; i < T::FRAG_M; ++i)
+    cA[i] = *reinterpret_cast<const i32x4_t*>(cur + ra * 64 + 16 * ((2 * s2 + h) ^ sw4) + i * 32 * 64);
+#pragma unroll
+  for (int j = 0; j < T::FRAG_N; ++j)
+    cB[j] = *reinterpret_cast<const i32x4_t*>(cur + rb * 64 + 16 * ((2 * s2 + h) ^ sw4) + j * 32 * 64);
+}
+
+template <class T, class D>
+__device__ __forceinline__ void mx_read_scales(const uint8_t* cur, int wm, int wn, int l32, int h,
+                                               uint32_t (&qA)[T::FRAG_M][2], uint32_t (&qB)[T::FRAG_N][2]) {
+  const int ra = wm * T::FRAG_M * 32 + l32, rb = T::BM + wn * T::FRAG_N * 32 + l32;
+#pragma unroll
+  for (int i = 0; i < T::FRAG_M; ++i) {
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (ra >> 2) * 16 + i * 8 * 16);
+    qA[i][0] = sq[h];
+    qA[i][1] = sq[2 + h];
+  }
+#pragma unroll
+  for (int j = 0; j < T::FRAG_N; ++j) {
+    const uint32_t* sq = reinterpret_cast<const uint32_t*>(cur + D::SCALE_OFF + (rb >> 2) * 16 + j * 8 * 16);
+    qB[j][0] = sq[h];
+    qB[j][1] = sq[2 + h];
+  }
+}
+
+template <int FM, int FN, int S2>
+__device__ __forceinline__ void mx_mma_half(float16_t (&acc)[FM][FN], const uint32_t (&sA)[FM],
+                                            const uint32_t (&sB)[FN], const i32x4_t (&cA)[FM],
+                                            const i32x4_t (&cB)[FN]) {
+  auto w = [](i32x4_t c) { return __builtin_shufflevector(c, c, 0, 1, 2, 3, -1, -1, -1, -1); };
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w(cB[j]), w(cA[i]), acc[i][j], 4, 4, S2, sB[j], S2,
                                                                   sA[i]);
 }
 
@@ -250,7 +270,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
     return;
   }
 
-  // The first S - 1 K-steps are issued up front (past the last one, the last is reloaded).
+  // Interleaved loop: the barrier of K-step kt sits between its two halves.  Before it, the first
+  // half's matrix instructions run while the second half's codes are read and K-step kt + S - 1 is
+  // fetched; after it, the second half runs while the scales and first-half codes of kt + 1 are read.
+  // Past the last K-step the last one is reloaded and a stale slot is read (values unused), so
+  // every step issues the same loads and waits on the same vmcnt.
 #pragma unroll
   for (int j = 0; j < S - 1; ++j) {
     const int kj = min(j, nkt - 1);
@@ -258,21 +282,45 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mx_kernel(
                  s_off, s_stride);
   }
   vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step 0 has landed
+  uint32_t qA[FM][2], qB[FN][2];
+  i32x4_t c0A[FM], c0B[FN], c1A[FM], c1B[FN];
+  mx_read_scales<T, D>(lds, wm, wn, l32, h, qA, qB);
+  mx_read_codes<T, D>(lds, wm, wn, l32, h, 0, c0A, c0B);
   int slot = 0;
   for (int kt = 0; kt < nkt; ++kt) {
-    const int slot2 = slot == 0 ? S - 1 : slot - 1;  // (kt + S - 1) % S: read in K-step kt - 1, now free
-    const int kn = min(kt + S - 1, nkt - 1);
-    dma_issue<D>(lds + slot2 * D::STAGE, wave, (uint32_t)kn * (BK / 2), (size_t)kn * (BK / 32), c_base, c_off, s_base,
-                 s_off, s_stride);
     uint32_t sA[FM], sB[FN];
-    i32x4_t cA[2][FM], cB[2][FN];
-    mx_read<T, D>(lds + slot * D::STAGE, wm, wn, l32, h, psel, sA, sB, cA, cB);
-    mx_mma(acc, sA, sB, cA, cB);
-    vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step kt + 1 has landed
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sA[i] = __builtin_amdgcn_perm(qA[i][1], qA[i][0], psel);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sB[j] = __builtin_amdgcn_perm(qB[j][1], qB[j][0], psel);
+    const uint8_t* cur = lds + slot * D::STAGE;
+    mx_mma_half<FM, FN, 0>(acc, sA, sB, c0A, c0B);
+    mx_read_codes<T, D>(cur, wm, wn, l32, h, 1, c1A, c1B);
+    const int slot2 = slot == 0 ? S - 1 : slot - 1;  // read in K-step kt - 1, free since its barrier
+    const int kn = min(kt + S - 1, nkt - 1);
+    dma_issue<D>(lds + slot2 * D::STAGE, wave, (uint32_t)kn * (BK / 2), (size_t)kn * (BK / 32), c_base, c_off,
+                 s_base, s_off, s_stride);
+#pragma unroll
+    for (int g = 0; g < FM * FN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct load
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait_barrier<(S - 2) * D::LOADS>();  // K-step kt + 1 has landed; slot kt is read
+    __builtin_amdgcn_sched_barrier(0);
     slot = slot == S - 1 ? 0 : slot + 1;
+    const uint8_t* nxt = lds + slot * D::STAGE;
+    mx_mma_half<FM, FN, 1>(acc, sA, sB, c1A, c1B);
+    mx_read_scales<T, D>(nxt, wm, wn, l32, h, qA, qB);
+    mx_read_codes<T, D>(nxt, wm, wn, l32, h, 0, c0A, c0B);
+#pragma unroll
+    for (int g = 0; g < FM * FN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+    }
   }
   vm_wait_barrier<0>();
-
   epilogue<T, LORA>(acc, lds, t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias, y);
 }
 

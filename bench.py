@@ -134,9 +134,15 @@ def sleep_cycles(torch, stream, seconds):
 
 def smi_state(flags):
     """rocm-smi's fields for the given query flags (power, performance level, clocks), or None."""
+    import shutil
     import subprocess
     try:
-        out = subprocess.run(["rocm-smi"] + flags + ["--json"], capture_output=True, text=True, timeout=20).stdout
+        # rocm-smi is a Python script: run it with this interpreter rather than through its
+        # "#!/usr/bin/env" line, so that no process replaces itself (under a profiler every child
+        # process has initialised the GPU before its first instruction)
+        tool = os.path.realpath(shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi")
+        cmd = [sys.executable, tool] if tool.endswith(".py") else [tool]
+        out = subprocess.run(cmd + flags + ["--json"], capture_output=True, text=True, timeout=20).stdout
         card = next(iter(json.loads(out).values()))
         return {k: v for k, v in card.items() if any(w in k.lower() for w in ("power", "perf", "sclk", "mclk", "fclk"))}
     except Exception:  # pragma: no cover - tool missing or unparsable output

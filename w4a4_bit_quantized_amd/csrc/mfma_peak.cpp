@@ -29,7 +29,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-enum Kind { FP4_32x32x64 = 0, FP4_16x16x128 = 1, FP8_32x32x64 = 2, F16_32x32x16 = 3 };
+enum Kind { FP4_32x32x64 = 0, FP4_16x16x128 = 1, FP8_32x32x64 = 2, F16_32x32x16 = 3, FP8_GROUP16 = 4 };
+
+// FP8_GROUP16 is the inner loop of the rejected route for 16-wide e4m3 scales: the E2M1 codes as
+// fp8 (exact), one fp8 32x32x16 instruction per 16-column group into a zeroed accumulator, then
+// every accumulator element scaled by its group's activation x weight scale and added to the
+// running sum in f32 (one multiply and one fused multiply-add per element and group).
 
 template <int KIND>
 __global__ __launch_bounds__(256) void probe(const int* in, float* out, unsigned long long* cyc, int iters) {
@@ -41,6 +46,11 @@ __global__ __launch_bounds__(256) void probe(const int* in, float* out, unsigned
   half8_t h8;
   for (int i = 0; i < 8; ++i) h8[i] = (_Float16)(in[l + i] & 7);
   const int s = 127 | (127 << 8);  // E8M0 scale 1.0 in the bytes the instructions select
+  const long a64 = (long)(((unsigned long)(unsigned)in[l] << 32) | (unsigned)in[l + 1]);
+  const long b64 = (long)(((unsigned long)(unsigned)in[l + 2] << 32) | (unsigned)in[l + 3]);
+  float sa[16];  // per-element activation scales of the lane's 16 rows (one per group in the real loop)
+  for (int r = 0; r < 16; ++r) sa[r] = 1.0f + (float)((in[l + r] >> 8) & 7) * 0.125f;
+  float sw = 1.0f + (float)(in[l] & 7) * 0.125f;  // the lane's column scale, changed every group
   f32x16_t c[8];
   f32x4_t d[8];
   for (int i = 0; i < 8; ++i) {
@@ -56,6 +66,12 @@ __global__ __launch_bounds__(256) void probe(const int* in, float* out, unsigned
       if (KIND == FP4_16x16x128) d[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, d[i], 4, 4, 0, s, 0, s);
       if (KIND == FP8_32x32x64) c[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, c[i], 0, 0, 0, s, 0, s);
       if (KIND == F16_32x32x16) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(h8, h8, c[i], 0, 0, 0);
+      if (KIND == FP8_GROUP16) {
+        const f32x16_t p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a64 ^ (long)i, b64, f32x16_t{}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[i][r] = __builtin_fmaf(p[r], sa[r] * sw, c[i][r]);
+        sw = sw * 1.0000001f;  // the next group's scale (never repeats, so no product can be reused)
+      }
     }
   }
   const unsigned long long t1 = clock64();
@@ -123,8 +139,9 @@ bool run(const char* name, const int* in, float* out, unsigned long long* cyc, i
   for (auto v : h) avg += (double)v;
   avg /= blocks;
   const double n = (double)iters * 8;
-  const double flops = KIND == FP4_16x16x128 ? 2.0 * 16 * 16 * 128 : KIND == F16_32x32x16 ? 2.0 * 32 * 32 * 16
-                                                                                           : 2.0 * 32 * 32 * 64;
+  const double flops = KIND == FP4_16x16x128                          ? 2.0 * 16 * 16 * 128
+                       : (KIND == F16_32x32x16 || KIND == FP8_GROUP16) ? 2.0 * 32 * 32 * 16
+                                                                       : 2.0 * 32 * 32 * 64;
   std::printf("%-26s %5.1f cycles/instr/wave  %7.3f ms  %8.1f TFLOP/s  clock %.2f GHz\n", name, avg / n, ms,
               flops * n * 4 * blocks / (ms * 1e-3) / 1e12, avg / (ms * 1e-3) / 1e9);
   (void)hipEventDestroy(e0);
@@ -162,7 +179,8 @@ int main(int argc, char** argv) {
     if (!run<FP4_32x32x64>("fp4 32x32x64 (scaled)", in, out, cyc, blocks, iters) ||
         !run<FP4_16x16x128>("fp4 16x16x128 (scaled)", in, out, cyc, blocks, iters) ||
         !run<FP8_32x32x64>("fp8 32x32x64 (scaled)", in, out, cyc, blocks, iters) ||
-        !run<F16_32x32x16>("f16 32x32x16", in, out, cyc, blocks, iters))
+        !run<F16_32x32x16>("f16 32x32x16", in, out, cyc, blocks, iters) ||
+        !run<FP8_GROUP16>("fp8 32x32x16 + f32 rescale", in, out, cyc, blocks, iters))
       return 1;
   }
   (void)hipFree(in);

@@ -85,6 +85,39 @@ __device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int r_lo, 
   if (!LORA) return;
   constexpr int LI = (T::BM * 16 + T::THREADS - 1) / T::THREADS;
   constexpr int PI = (T::BN * 16 + T::THREADS - 1) / T::THREADS;
+  if constexpr ((T::BM * 16) % T::THREADS == 0 && (T::BN * 16) % T::THREADS == 0) {
+    // A tile wholly inside M x N with a rank that is a multiple of 16: nothing is clamped or
+    // masked, so every element's offset is one per-thread base plus an immediate.
+    if (m0 + T::BM <= M && n0 + T::BN <= N && (R & 15) == 0 && r_hi <= R) {
+      constexpr int RSTEP = T::THREADS / 16;  // rows per u
+      const int tr = t >> 4, tc = t & 15;
+      const float* lb = lora + (size_t)(m0 + tr) * R + tc;
+      const uint16_t* pb = pu + (size_t)(n0 + tr) * R + tc;
+      const size_t part = (size_t)M * R;
+      for (int r0 = r_lo; r0 < r_hi; r0 += 16) {
+        float f[LI];
+        uint32_t pw[PI];
+#pragma unroll
+        for (int u = 0; u < LI; ++u) {
+          float acc_l = 0.0f;
+          for (int p = 0; p < parts; ++p) acc_l += lb[p * part + u * RSTEP * R + r0];
+          f[u] = acc_l;
+        }
+#pragma unroll
+        for (int u = 0; u < PI; ++u) pw[u] = pb[u * RSTEP * R + r0];
+#pragma unroll
+        for (int u = 0; u < LI; ++u) {
+          const int rr = tr + u * RSTEP, r = r0 - r_lo + tc;
+          const uint32_t hb = f32_to_bf16_bits(f[u]);
+          l_hi[rr * rs + r] = (uint16_t)hb;
+          l_lo[rr * rs + r] = (uint16_t)f32_to_bf16_bits(f[u] - bf16_bits_to_f32(hb));  // exact remainder
+        }
+#pragma unroll
+        for (int u = 0; u < PI; ++u) p_lds[(tr + u * RSTEP) * rs + r0 - r_lo + tc] = (uint16_t)pw[u];
+      }
+      return;
+    }
+  }
   for (int r0 = r_lo; r0 < r_hi; r0 += 16) {
     float f[LI];
     uint32_t pw[PI];

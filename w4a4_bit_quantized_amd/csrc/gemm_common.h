@@ -86,23 +86,20 @@ __device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int r_lo, 
   constexpr int LI = (T::BM * 16 + T::THREADS - 1) / T::THREADS;
   constexpr int PI = (T::BN * 16 + T::THREADS - 1) / T::THREADS;
   if constexpr ((T::BM * 16) % T::THREADS == 0 && (T::BN * 16) % T::THREADS == 0) {
-    // A tile wholly inside M x N with a rank that is a multiple of 16: nothing is clamped or
-    // masked, so every element's offset is one per-thread base plus an immediate.
-    if (m0 + T::BM <= M && n0 + T::BN <= N && (R & 15) == 0 && r_hi <= R) {
+    // A tile wholly inside M x N with one partial sum and a rank that is a multiple of 16:
+    // nothing is clamped, masked or summed, so every element's offset is one per-thread base plus
+    // an immediate.  (Several partial sums come only with batches of at most 32 rows, whose
+    // tiles are never wholly inside M.)
+    if (m0 + T::BM <= M && n0 + T::BN <= N && parts == 1 && (R & 15) == 0 && r_hi <= R) {
       constexpr int RSTEP = T::THREADS / 16;  // rows per u
       const int tr = t >> 4, tc = t & 15;
       const float* lb = lora + (size_t)(m0 + tr) * R + tc;
       const uint16_t* pb = pu + (size_t)(n0 + tr) * R + tc;
-      const size_t part = (size_t)M * R;
       for (int r0 = r_lo; r0 < r_hi; r0 += 16) {
         float f[LI];
         uint32_t pw[PI];
 #pragma unroll
-        for (int u = 0; u < LI; ++u) {
-          float acc_l = 0.0f;
-          for (int p = 0; p < parts; ++p) acc_l += lb[p * part + u * RSTEP * R + r0];
-          f[u] = acc_l;
-        }
+        for (int u = 0; u < LI; ++u) f[u] = lb[u * RSTEP * R + r0];
 #pragma unroll
         for (int u = 0; u < PI; ++u) pw[u] = pb[u * RSTEP * R + r0];
 #pragma unroll

@@ -102,12 +102,19 @@ __device__ __forceinline__ void stage_epilogue(uint8_t* base, int rs, int r_lo, 
         for (int u = 0; u < LI; ++u) f[u] = lb[u * RSTEP * R + r0];
 #pragma unroll
         for (int u = 0; u < PI; ++u) pw[u] = pb[u * RSTEP * R + r0];
+        // hi + lo split of two rows at a time with the hardware convert (nearest even)
+        static_assert(LI % 2 == 0, "row pairs");
 #pragma unroll
-        for (int u = 0; u < LI; ++u) {
+        for (int u = 0; u < LI; u += 2) {
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{f[u], f[u + 1]}, bf16x2_t));
+          const float e0 = f[u] - __uint_as_float(hp << 16), e1 = f[u + 1] - __uint_as_float(hp & 0xFFFF0000u);
+          const uint32_t lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{e0, e1}, bf16x2_t));
           const int rr = tr + u * RSTEP, r = r0 - r_lo + tc;
-          const uint32_t hb = f32_to_bf16_bits(f[u]);
-          l_hi[rr * rs + r] = (uint16_t)hb;
-          l_lo[rr * rs + r] = (uint16_t)f32_to_bf16_bits(f[u] - bf16_bits_to_f32(hb));  // exact remainder
+          l_hi[rr * rs + r] = (uint16_t)hp;
+          l_hi[(rr + RSTEP) * rs + r] = (uint16_t)(hp >> 16);
+          l_lo[rr * rs + r] = (uint16_t)lp;  // the exact remainder, rounded
+          l_lo[(rr + RSTEP) * rs + r] = (uint16_t)(lp >> 16);
         }
 #pragma unroll
         for (int u = 0; u < PI; ++u) p_lds[(tr + u * RSTEP) * rs + r0 - r_lo + tc] = (uint16_t)pw[u];

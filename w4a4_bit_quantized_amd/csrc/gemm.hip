@@ -502,7 +502,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(
 // the same grouped, XCD-aware order (gridDim.x a multiple of 8 keeps every tile of a workgroup
 // on one XCD).  The epilogue operands live in a region E after stage slots 0 and 1, staged 32
 // ranks at a time, so the next tile's K-steps 0 and 1 are fetched into those slots as soon as
-// the first pass is staged and land while the epilogue computes.  y leaves through buffer
+// the K loop ends (before the operands are staged) and land while the epilogue computes.  y leaves through buffer
 // stores: a chunk outside y gets an offset the hardware drops, so every wave issues exactly ST
 // stores per tile (before the first tile, ST dropped ones), and each tile's first waits count
 // them in: the stores drain while K-steps 0 and 1 run on the matrix cores.  Loads and stores
@@ -560,8 +560,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_persist_kerne
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     dma_k_loop<T, P::ST>(acc, lds, ad, wave, wm, wn, l32, h, nkt);
 
-    // epilogue; once its first operand pass is staged, the next tile's K-steps 0 and 1 go into
-    // slots 0 and 1
+    // epilogue; first the next tile's K-steps 0 and 1 go into slots 0 and 1
     asm volatile("" : "+v"(lane));
     const int vn = v + (int)gridDim.x;
     const bool more = vn < tiles;  // workgroup-uniform

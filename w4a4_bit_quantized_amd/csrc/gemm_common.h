@@ -433,8 +433,8 @@ __device__ __forceinline__ void drop_stores(__amdgpu_buffer_rsrc_t yr) {
 __device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Epilogue of one tile in the persistent kernels (as `epilogue`, whole-tile form): the operands are
-// staged in a region E after stage slots 0 and 1, 32 ranks per pass; `prefetch` runs once the first
-// pass is staged (it issues the next tile's first K-steps into slots 0 and 1); y leaves through
+// staged in a region E after stage slots 0 and 1, 32 ranks per pass; `prefetch` runs first (it
+// issues the next tile's first K-steps into slots 0 and 1); y leaves through
 // exactly P::ST buffer stores per wave, chunks outside y at an offset the hardware drops.
 template <class T, class P, bool LORA, class Prefetch>
 __device__ __forceinline__ void persist_epilogue(float16_t (&acc)[T::FRAG_M][T::FRAG_N], uint8_t* lds, int wave, int lane,
@@ -455,9 +455,11 @@ __device__ __forceinline__ void persist_epilogue(float16_t (&acc)[T::FRAG_M][T::
   const uint16_t* p_lds = l_lo + T::BM * rs;
   const float* c_lds = reinterpret_cast<const float*>(p_lds + T::BN * rs);
   const float* b_lds = c_lds + T::BN;
-  // epilogue operands, first pass; then the caller's prefetch of the next tile
-  stage_epilogue<T, LORA>(E, rs, 0, min(rp, rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
+  // the caller's prefetch of the next tile's first K-steps into slots 0 and 1 (free since the K
+  // loop's last barrier), then the epilogue operands' first pass into E, whose loads wait out
+  // the same latency
   prefetch();
+  stage_epilogue<T, LORA>(E, rs, 0, min(rp, rw), t, m0, n0, M, N, R, parts, lora, pu, wcs, wts, bias);
   lds_only_barrier();
 
   // acc *= wcscales * wtscale; + L @ proj_up^T (passes of 32 ranks); + bias (as in `epilogue`)

@@ -1,18 +1,25 @@
 """Exactness of the quantizer's two fast divisions (CPU, exact rational arithmetic).
 
-The activation quantizer never issues a divide instruction per element.  Both of its divisions
-use one reciprocal r = RN(1/d) and one Markstein correction, each step a single IEEE float32
-rounding (the two corrections are fused multiply-adds, rounded once):
-
-    q0 = RN(x * r);   e = RN(q0 * d - x);   q = RN(q0 - e * r)
+The activation quantizer never issues a divide instruction per element:
 
 * smoothing, x / lambda (rotate notes section 1 and the "SVDQuant W4A4" page's smooth_factor):
-  x and lambda are bf16, r = RN(1/lambda) is computed once per column.  Claim: q == RN(x/lambda)
-  bit for bit whenever 2^-64 <= |x| < 2^96 (or x = +-0) and 2^-32 <= lambda <= 2^32 (the kernel
-  takes the IEEE division for any wave holding an input outside this range).
+  x and lambda are bf16; lambda = m 2^E with m one of 128 significands.  A table holds, per m,
+  rh = RD(1/m) and rl = RN((1 - m rh) rh) (the residual 1 - m rh is exact and >= 0); per column
+  the kernel scales both by 2^-E (exact), and per element it computes
+
+      q = RN(x * rh + RN(x * rl))       (a multiply, then a fused multiply-add)
+
+  Claim: q == RN(x/lambda) bit for bit, signed zeros included, whenever 2^-64 <= |x| < 2^96 (or
+  x = +-0) and 2^-32 <= lambda <= 2^32 (the kernel takes the IEEE division for any wave holding
+  an input outside this range).
 * group quantization, v / sd (rotate notes section 1: q = round(x / scale)): v is any float32,
-  sd a nonzero e4m3 scale and r = RN(1/sd) comes from a 128-entry table.  Claim: the E2M1 code
-  of q equals the code of RN(v/sd) for every finite v.
+  sd a nonzero e4m3 scale, r = RN(1/sd) comes from a 128-entry table and one Markstein
+  correction follows, each step a single IEEE float32 rounding (the corrections are fused
+  multiply-adds, rounded once):
+
+      q0 = RN(v * r);   e = RN(q0 * sd - v);   q = RN(q0 - e * r)
+
+  Claim: the E2M1 code of q equals the code of RN(v/sd) for every finite v.
 
 Every step below is emulated with Python Fractions and an exact round-to-nearest-even to
 float32 (normal and subnormal), so nothing here runs the kernel's arithmetic in float32.
@@ -109,41 +116,103 @@ def _bf16_values(lo_exp, hi_exp):
     return [F(m, 128) * TWO ** e for e in range(lo_exp, hi_exp + 1) for m in range(128, 256)]
 
 
+def _prev32(v):
+    """The float32 value just below the positive normal float32 v (its bit pattern minus one)."""
+    return F(float(np.nextafter(np.float32(float(v)), np.float32(0))))
+
+
+def recip_parts(lam):
+    """(rh, rl) of a bf16 lambda = m 2^E as the kernel forms them: the table entry of m, built
+    with one IEEE division, a round-down step and the exact residual, scaled by 2^-E."""
+    e_ = 0
+    m = lam
+    while m >= 2:
+        m, e_ = m / 2, e_ + 1
+    while m < 1:
+        m, e_ = m * 2, e_ - 1
+    rh = rn32(1 / m)
+    if rn32(1 - m * rh) < 0:  # the kernel's test: fma(-m, rh, 1) < 0
+        rh = _prev32(rh)
+    res = 1 - m * rh
+    assert res >= 0 and rn32(res) == res, "the residual of a round-down reciprocal is exact"
+    rl = rn32(res * rh)
+    return rh * TWO ** -e_, rl * TWO ** -e_
+
+
+def smooth_div(x, lam, parts=None):
+    """The kernel's smoothing quotient: RN(x rh + RN(x rl))."""
+    rh, rl = parts or recip_parts(lam)
+    return rn32(x * rh + rn32(x * rl))
+
+
+def smooth_div_signed(x, lam):
+    """smooth_div() on (value, negative) pairs: the sign of a zero result is tracked (rh > 0 and
+    rl >= 0, so x * rl is a zero of x's sign when x is zero)."""
+    rh, rl = recip_parts(lam)
+    t = rn32(x[0] * rl)
+    return _fma_signed(x, (rh, False), (t, x[1] if t == 0 else t < 0))
+
+
+def test_reciprocal_table_entries():
+    """For each of the 128 bf16 significands m: rh = RD(1/m) (never above 1/m, within one ulp),
+    the residual 1 - m rh exact and non-negative (asserted inside recip_parts), and rh + rl
+    within 2^-46 of 1/m: the two-part reciprocal the per-element sequence relies on."""
+    for k in range(128, 256):
+        m = F(k, 128)
+        rh, rl = recip_parts(m)
+        assert rh <= 1 / m < rh + TWO ** -23
+        assert rl >= 0
+        assert abs(rh + rl - 1 / m) <= TWO ** -46 / m
+
+
 def test_smoothing_division_exact_over_every_bf16_mantissa_pair():
     """Every pair of bf16 significands (x in [1, 2), lambda in [1, 2)): q == RN(x / lambda).
-    Within the stated ranges every intermediate is a normal float32, so each step commutes with
-    scaling x by 2^a and lambda by 2^b; the pairs therefore cover all exponents.  The sequence
-    is odd in x, so negative x follow; the sign of zero is checked separately."""
+    Within the stated ranges the quotient and x rh are normal float32 values and RN(x rl) errs by
+    far less than the quotient's distance to a rounding midpoint (a quotient of two 8-bit
+    significands is exact or at least 2^-33 of its size away from every float32 midpoint, while
+    rh + rl and the rounding of x rl stay within 2^-45 of it), so the pairs cover all exponents;
+    the corners of the range are checked directly below.  The sequence is odd in x, so negative
+    x follow; the sign of zero is checked separately."""
     xs = _bf16_values(0, 0)
     bad = []
     for lam in xs:
-        r = rn32(1 / lam)
+        parts = recip_parts(lam)
         for x in xs:
-            if markstein(x, lam, r) != rn32(x / lam):
+            if smooth_div(x, lam, parts) != rn32(x / lam):
                 bad.append((x, lam))
     assert not bad, f"{len(bad)} pairs differ, first {bad[:3]}"
 
 
 @pytest.mark.parametrize("xe,le", [(-64, 32), (95, -32), (-64, -32), (95, 32), (40, 7), (-20, -5)])
 def test_smoothing_division_exact_at_the_range_ends(xe, le):
-    """The scaling argument checked directly at the corners of the stated range (|x| = 2^-64 ..
-    2^96, lambda = 2^-32 .. 2^32): every x significand against a stride of lambda significands."""
+    """The corners of the stated range (|x| = 2^-64 .. 2^96, lambda = 2^-32 .. 2^32), where x rl
+    can be subnormal: every x significand against a stride of lambda significands."""
     lam_e = le if le < 32 else 31  # lambda <= 2^32: significands of the binade below, and 2^32 itself
     lams = [F(m, 128) * TWO ** lam_e for m in range(128, 256, 5)] + [TWO ** le]
     for lam in lams:
-        r = rn32(1 / lam)
+        parts = recip_parts(lam)
         for m in range(128, 256):
             x = F(m, 128) * TWO ** xe
-            assert markstein(x, lam, r) == rn32(x / lam), (x, lam)
-            assert markstein(-x, lam, r) == -rn32(x / lam), (-x, lam)
+            assert smooth_div(x, lam, parts) == rn32(x / lam), (x, lam)
+            assert smooth_div(-x, lam, parts) == -rn32(x / lam), (-x, lam)
 
 
 def test_smoothing_division_signed_zero():
     """x = +0 gives +0 and x = -0 gives -0, as the IEEE division does (lambda > 0)."""
-    for lam in (F(1), F(3, 2), TWO ** -32, TWO ** 32):
-        r = rn32(1 / lam)
+    for lam in (F(1), F(3, 2), F(255, 128), TWO ** -32, TWO ** 32):
         for neg in (False, True):
-            assert markstein_signed((F(0), neg), lam, r) == (F(0), neg)
+            assert smooth_div_signed((F(0), neg), lam) == (F(0), neg)
+
+
+def test_smoothing_sequence_is_not_exact_with_rounded_reciprocal_alone():
+    """Planted-mistake check of the proof itself: with only rh (rl dropped) some pairs round
+    differently, so the exhaustive test above does detect a wrong sequence."""
+    xs = _bf16_values(0, 0)
+    diff = 0
+    for lam in xs[::7]:
+        rh, _ = recip_parts(lam)
+        diff += sum(rn32(x * rh) != rn32(x / lam) for x in xs)
+    assert diff > 0
 
 
 E2M1_POINTS = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]

@@ -20,19 +20,25 @@
 // a - b, a second swap returns the results); span 64 joins the two steps of a
 // 128-column unit.
 //
-// Division.  Both divisions are correctly rounded.  x / lambda uses the
-// reciprocal r = RN(1/lambda) (one IEEE division per column, computed once per
-// unit and shared through LDS) and one Markstein correction:
-//   q0 = RN(x r),  e = RN(q0 lambda - x) (exact, fused),  q = RN(q0 - e r).
-// For bf16 x with 2^-64 <= |x| < 2^96 (or x = +-0) and bf16 lambda in
-// [2^-32, 2^32] this equals RN(x / lambda) bit for bit, signed zeros included
-// (checked exhaustively over every such pair of bf16 mantissas and exponent
+// Division.  Both divisions are correctly rounded without a divide instruction
+// per element.  x / lambda uses a two-part reciprocal of lambda = m 2^E (m the
+// bf16 mantissa, one of 128 values): rh = RD(1/m) 2^-E and rl = RN((1 - m RD(1/m))
+// RD(1/m)) 2^-E, both from a 128-entry table built once per workgroup (the
+// residual 1 - m RD(1/m) is exact and >= 0), then per element
+//   q = RN(x rh + RN(x rl))   (one multiply and one fused multiply-add).
+// rh + rl is within 2^-46 of 1/lambda, and a quotient of two 8-bit mantissas is
+// either a float32 or farther than that from every rounding midpoint, so for
+// bf16 x with 2^-64 <= |x| < 2^96 (or x = +-0; rl >= 0 keeps the sign of a zero)
+// and bf16 lambda in [2^-32, 2^32] this equals RN(x / lambda) bit for bit
+// (checked exhaustively over every pair of bf16 mantissas and the exponent
 // offsets); units or waves whose inputs fall outside that range take the IEEE
-// division instead.  v / sd uses the same sequence with r = RN(1/sd) from a
-// 128-entry table; there the E2M1 code of the result equals the code of the
-// IEEE quotient for every finite v and every nonzero e4m3 sd reachable from the
-// group maximum (checked near every decision point and across all binades);
-// groups whose maximum is not finite take the IEEE division.
+// division instead.  v / sd uses r = RN(1/sd) from a 128-entry table and one
+// Markstein correction,
+//   q0 = RN(v r),  e = RN(q0 sd - v) (exact, fused),  q = RN(q0 - e r);
+// there the E2M1 code of the result equals the code of the IEEE quotient for
+// every finite v and every nonzero e4m3 sd reachable from the group maximum
+// (checked near every decision point and across all binades); groups whose
+// maximum is not finite take the IEEE division.
 //
 // Low-rank down-projection.  x_s is split into a bf16 high part and a bf16 low
 // part (x_s = hi + lo to about 16 significant bits) that feed the 16x16x32 bf16
@@ -68,11 +74,12 @@ struct QCfg {
   static constexpr int RS = RP + 16;               // LDS row stride of proj_down (u16), 32 bytes of padding
   static constexpr int WAVES = max_waves(HB, RB);  // most waves per workgroup (register budget)
   static constexpr int PD_BYTES = (ACT && RB > 0) ? 64 * RS * 2 : 0;
-  static constexpr int LAM_BYTES = ACT ? 2 * UC * 4 : 0;
+  static constexpr int LAM_BYTES = ACT ? 3 * UC * 4 : 0;   // lambda, rh, rl of the unit's columns
   static constexpr int WAVE_BYTES = PD_BYTES + LAM_BYTES;
   static constexpr int RED_BYTES = (ACT && RB > 0) ? WAVES * QROWS * RP * 4 : 0;
   static constexpr int BODY_BYTES = WAVES * WAVE_BYTES > RED_BYTES ? WAVES * WAVE_BYTES : RED_BYTES;
-  static constexpr int LDS_BYTES = 512 + BODY_BYTES;  // 128-entry reciprocal table first
+  static constexpr int TAB_BYTES = 512 + 1024;       // reciprocals of the e4m3 scales, then (rh, rl) of the bf16 mantissas
+  static constexpr int LDS_BYTES = TAB_BYTES + BODY_BYTES;
 };
 
 template <int HB>
@@ -149,7 +156,7 @@ __device__ __forceinline__ void fwht_unit(float (&v)[US][16]) {
     for (int i = 0; i < 16; ++i) v[c][i] = v[c][i] * cb;
 }
 
-// x / d correctly rounded for the operand ranges stated at the top of the file.
+// v / d with the E2M1 code of the IEEE quotient (see the top of the file).
 __device__ __forceinline__ float div_markstein(float x, float d, float r) {
   const float q0 = x * r;
   const float e = fmaf(q0, d, -x);
@@ -266,13 +273,23 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
   const uint16_t* xrow = x + (size_t)(row_ok ? m : m0) * K;
   uint8_t* qrow = q + (size_t)(row_ok ? m : m0) * qstride;
 
-  uint8_t* wbase = smem + 512 + wave * C::WAVE_BYTES;
+  float2_t* mtab = reinterpret_cast<float2_t*>(smem + 512);
+  uint8_t* wbase = smem + C::TAB_BYTES + wave * C::WAVE_BYTES;
   float* lam_s = reinterpret_cast<float*>(wbase + C::PD_BYTES);
-  float* rlam_s = lam_s + UC;
+  float* rh_s = lam_s + UC;
+  float* rl_s = lam_s + 2 * UC;
   uint16_t* pd_s = reinterpret_cast<uint16_t*>(wbase);
 
   for (int b = threadIdx.x; b < 128; b += blockDim.x)
     rtab[b] = (b == 0 || b == 127) ? 0.0f : __fdiv_rn(1.0f, e4m3_decode((uint32_t)b));
+  if constexpr (ACT) {
+    for (int b = threadIdx.x; b < 128; b += blockDim.x) {
+      const float mm = __uint_as_float(0x3F800000u | ((uint32_t)b << 16));  // 1 + b/128
+      float rh = __fdiv_rn(1.0f, mm);
+      if (fmaf(-mm, rh, 1.0f) < 0.0f) rh = __uint_as_float(__float_as_uint(rh) - 1u);  // RD(1/mm)
+      mtab[b] = float2_t{rh, fmaf(-mm, rh, 1.0f) * rh};  // the residual is exact and >= 0
+    }
+  }
   __syncthreads();
 
   // blockIdx.y selects a contiguous part of the units (K split across workgroups for small M;
@@ -372,14 +389,18 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
 
     float v[US][16];
     if constexpr (ACT) {
-      // lambda and RN(1/lambda) of the unit's columns, shared through the wave's LDS
+      // lambda and its two-part reciprocal (rh, rl) of the unit's columns, shared through the
+      // wave's LDS; lambda = m 2^E in range scales the mantissa's table entry by 2^-E exactly
       bool lam_ok = true;
 #pragma unroll
       for (int c = 0; c < US; ++c) {
         const float lf = bf16_bits_to_f32(lac[c]);
         lam_ok &= (lf >= 0x1p-32f) && (lf <= 0x1p32f);
+        const float2_t t = mtab[lac[c] & 0x7Fu];
+        const float p2 = __uint_as_float((254u << 23) - (__float_as_uint(lf) & 0x7F800000u));  // 2^-E
         lam_s[64 * c + lane] = lf;
-        rlam_s[64 * c + lane] = __fdiv_rn(1.0f, lf);
+        rh_s[64 * c + lane] = t[0] * p2;
+        rl_s[64 * c + lane] = t[1] * p2;
       }
       u16x2_t mn = {0xFFFFu, 0xFFFFu}, mx = {0u, 0u};
 #pragma unroll
@@ -392,27 +413,36 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
       wave_lds_sync();
 #pragma unroll
       for (int c = 0; c < US; ++c) {
-        const float* ls = lam_s + 64 * c + 16 * qd;
-        const float* rl = rlam_s + 64 * c + 16 * qd;
-        float lv[16], rv[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4_t a = *reinterpret_cast<const float4_t*>(ls + 4 * i);
-          const float4_t b = *reinterpret_cast<const float4_t*>(rl + 4 * i);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { lv[4 * i + e] = a[e]; rv[4 * i + e] = b[e]; }
-        }
         if (fast) {
+          const float* ph = rh_s + 64 * c + 16 * qd;
+          const float* pl = rl_s + 64 * c + 16 * qd;
+          float hv[16], lw[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4_t a = *reinterpret_cast<const float4_t*>(ph + 4 * i);
+            const float4_t b = *reinterpret_cast<const float4_t*>(pl + 4 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { hv[4 * i + e] = a[e]; lw[4 * i + e] = b[e]; }
+          }
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const uint32_t d = xc[c][h][i];
               const int j = 8 * h + 2 * i;
-              v[c][j] = div_markstein(__uint_as_float(d << 16), lv[j], rv[j]);
-              v[c][j + 1] = div_markstein(__uint_as_float(d & 0xFFFF0000u), lv[j + 1], rv[j + 1]);
+              const float x0 = __uint_as_float(d << 16), x1 = __uint_as_float(d & 0xFFFF0000u);
+              v[c][j] = fmaf(x0, hv[j], x0 * lw[j]);
+              v[c][j + 1] = fmaf(x1, hv[j + 1], x1 * lw[j + 1]);
             }
         } else {  // inputs outside the proven range somewhere in the wave: IEEE division
+          const float* ls = lam_s + 64 * c + 16 * qd;
+          float lv[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4_t a = *reinterpret_cast<const float4_t*>(ls + 4 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lv[4 * i + e] = a[e];
+          }
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -513,7 +543,7 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
   if constexpr (LORA) {
     // ---- deterministic cross-wave reduction of the low-rank partials ----------------------
     __syncthreads();  // every wave is done with its proj_down staging area
-    float* red = reinterpret_cast<float*>(smem + 512);
+    float* red = reinterpret_cast<float*>(smem + C::TAB_BYTES);
     float* my_red = red + wave * QROWS * RP;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)

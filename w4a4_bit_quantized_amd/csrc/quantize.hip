@@ -9,7 +9,10 @@
 //   s8  = e4m3(f32(amax|v| / 6)),  code = e2m1(f32(v / e4m3_value(s8))), 0 when s8 == 0
 //   lora_act = x_s @ proj_down (activations only; unrotated x_s)
 //
-// Work decomposition.  A workgroup owns 16 rows; its waves split K into
+// Work decomposition.  A workgroup owns 16 rows (consecutive workgroups go to the 8 XCDs in
+// turn, so workgroup b takes row block xcd_block(b): each XCD runs a contiguous range of row
+// blocks, and the 16-byte pieces that eight row blocks write into each 128-byte line of the
+// (K/16, M) scale rows meet in one L2 instead of eight); its waves split K into
 // contiguous runs of units (64 columns, or 128 for B = 128).  A unit is one or
 // two 64-column steps.  In a step, lane l holds row l % 16 and the 16
 // consecutive columns 16 * (l / 16) .. +16: exactly one quantization group, so
@@ -81,6 +84,13 @@ struct QCfg {
   static constexpr int TAB_BYTES = 512 + 1024;       // reciprocals of the e4m3 scales, then (rh, rl) of the bf16 mantissas
   static constexpr int LDS_BYTES = TAB_BYTES + BODY_BYTES;
 };
+
+// Row block of workgroup b of G when workgroups are dispatched to the 8 XCDs in turn: XCD x runs
+// a contiguous range of blocks (a bijection on [0, G) for any G).
+__device__ __forceinline__ int xcd_block(int b, int G) {
+  const int q = G / 8, r = G % 8, x = b % 8, l = b / 8;
+  return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+}
 
 template <int HB>
 __device__ __forceinline__ float hadamard_scale() {
@@ -265,7 +275,7 @@ __global__ __launch_bounds__(64 * max_waves(HB, RB)) void quantize_kernel(
   const int nwaves = blockDim.x >> 6;
   const int row = lane & 15;
   const int qd = lane >> 4;
-  const int m0 = blockIdx.x * QROWS;
+  const int m0 = xcd_block(blockIdx.x, gridDim.x) * QROWS;
   const int m = m0 + row;
   const bool row_ok = m < M;
   const size_t qstride = (size_t)K / 2;

@@ -11,7 +11,12 @@
 // HIP events over 5 repetitions after a warm-up (buffers far larger than the 256 MB Infinity
 // Cache).  LDS: every CU runs one workgroup of 256, 512 or 1024 threads reading 16 bytes per lane
 // per instruction from a 64 KB buffer, consecutive lanes on consecutive 16-byte chunks (no bank
-// conflicts), timed with HIP events.  Nothing here is part of the library.
+// conflicts), timed with HIP events.  L2 -> LDS: every CU runs one 1024-thread workgroup that
+// streams 32 KB per step from its own 64 KB window (resident in L2 after the first pass) through
+// three 32 KB LDS slots, two steps in flight, one barrier per step (the GEMMs' pipeline without
+// their arithmetic), once with direct loads into LDS (global_load_lds_dwordx4) and once with
+// 16-byte loads into registers followed by 16-byte LDS stores; wall time from HIP events, shader
+// cycles from s_memtime.  Nothing here is part of the library.
 //
 // Usage: mfma_peak [iterations]   (default 4000)
 
@@ -114,6 +119,67 @@ __global__ __launch_bounds__(THREADS) void lds_read(unsigned* out, int iters) {
       acc ^= *reinterpret_cast<const u32x4_t*>(lds + ((base + (unsigned)r * 1024u + (unsigned)(it & 3) * 16384u) & 0xFFF0u));
   }
   if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9E3779B9u) out[0] = 1;  // keeps the reads alive
+}
+
+// L2 -> LDS streaming (see the top of the file).  Every address lies in [src, src + gridDim.x * 64 KB)
+// and in [0, 96 KB) of LDS.
+constexpr int SL_STEP = 32768, SL_REGION = 65536;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__global__ __launch_bounds__(1024) void stream_direct(const unsigned char* __restrict__ src, int steps,
+                                                       unsigned long long* cyc) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[3 * SL_STEP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned char* base = src + (size_t)blockIdx.x * SL_REGION;
+  auto issue = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      __builtin_amdgcn_global_load_lds(base + (st & 1) * SL_STEP + (r * 16 + wave) * 1024 + lane * 16,
+                                       (lds_void_t*)(lds + (st % 3) * SL_STEP + (r * 16 + wave) * 1024), 16, 0, 0);
+  };
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  issue(0);
+  issue(1);
+  for (int st = 0; st < steps; ++st) {
+    asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");  // step st has landed
+    issue(st + 2);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) cyc[blockIdx.x] = (t1 - t0) | (lds[5] == 0xEE && lds[SL_STEP + 9] == 0x11 ? 1ull << 63 : 0);
+}
+
+__global__ __launch_bounds__(1024) void stream_regs(const unsigned char* __restrict__ src, int steps,
+                                                     unsigned long long* cyc) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[3 * SL_STEP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned char* base = src + (size_t)blockIdx.x * SL_REGION;
+  u32x4_t a[2], b[2];
+  auto ld = [&](int st, u32x4_t (&d)[2]) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      d[r] = *reinterpret_cast<const u32x4_t*>(base + (st & 1) * SL_STEP + (r * 16 + wave) * 1024 + lane * 16);
+  };
+  auto put = [&](int st, const u32x4_t (&d)[2]) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      *reinterpret_cast<u32x4_t*>(lds + (st % 3) * SL_STEP + (r * 16 + wave) * 1024 + lane * 16) = d[r];
+  };
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  ld(0, a);
+  ld(1, b);
+  for (int st = 0; st < steps; st += 2) {  // steps even
+    put(st, a);
+    __syncthreads();
+    ld(st + 2, a);
+    put(st + 1, b);
+    __syncthreads();
+    ld(st + 3, b);
+  }
+  __syncthreads();
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const bool keep = a[0][0] == 0xDEADBEEFu && b[1][3] == 7u && lds[5] == 0xEE;
+  if (threadIdx.x == 0) cyc[blockIdx.x] = (t1 - t0) | (keep ? 1ull << 63 : 0);
 }
 
 bool ok(hipError_t e, const char* what) {
@@ -239,6 +305,43 @@ int main(int argc, char** argv) {
     const double bytes = (double)threads * 16.0 * 16.0 * lds_iters * blocks;
     std::printf("%4d threads per CU %8.3f ms  %7.1f TB/s  %6.0f GB/s per CU\n", threads, ms, bytes / (ms * 1e-3) / 1e12,
                 bytes / blocks / (ms * 1e-3) / 1e9);
+  }
+  // L2 -> LDS streaming
+  {
+    const int steps = 4000;
+    unsigned char* src = nullptr;
+    unsigned long long* scyc = nullptr;
+    if (!ok(hipMalloc(&src, (size_t)blocks * SL_REGION), "alloc") ||
+        !ok(hipMalloc(&scyc, (size_t)blocks * sizeof(unsigned long long)), "alloc") ||
+        !ok(hipMemset(src, 1, (size_t)blocks * SL_REGION), "memset"))
+      return 1;
+    std::printf("L2 -> LDS (one 1024-thread workgroup per CU, 32 KB per step from a 64 KB window, 3 slots, %d steps)\n",
+                steps);
+    std::vector<unsigned long long> h(blocks);
+    for (int v = 0; v < 2; ++v) {
+      auto launch = [&] {
+        if (v == 0) hipLaunchKernelGGL(stream_direct, dim3(blocks), dim3(1024), 0, 0, src, steps, scyc);
+        else hipLaunchKernelGGL(stream_regs, dim3(blocks), dim3(1024), 0, 0, src, steps, scyc);
+      };
+      launch();  // warm-up (also brings every window into L2)
+      if (!ok(hipDeviceSynchronize(), "stream warm-up")) return 1;
+      (void)hipEventRecord(e0);
+      launch();
+      (void)hipEventRecord(e1);
+      if (!ok(hipEventSynchronize(e1), "stream run")) return 1;
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, e0, e1);
+      if (!ok(hipMemcpy(h.data(), scyc, (size_t)blocks * 8, hipMemcpyDeviceToHost), "copy")) return 1;
+      double cyc_avg = 0;
+      for (auto c : h) cyc_avg += (double)(c & ~(1ull << 63));
+      cyc_avg /= blocks;
+      const double per_cu = (double)SL_STEP * steps;
+      std::printf("%-26s %8.3f ms  %7.1f TB/s  %6.0f GB/s per CU  %5.1f bytes per CU and cycle\n",
+                  v == 0 ? "direct loads into LDS" : "register loads + LDS store", ms,
+                  per_cu * blocks / (ms * 1e-3) / 1e12, per_cu / (ms * 1e-3) / 1e9, per_cu / cyc_avg);
+    }
+    (void)hipFree(src);
+    (void)hipFree(scyc);
   }
   (void)hipFree(flag);
   return 0;
